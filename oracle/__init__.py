@@ -1,0 +1,16 @@
+"""fp64 CPU oracle for exact attention — test infrastructure only.
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg import this
+package; the HIP library and its binding never do. See ``oracle.attention``.
+"""
+from .attention import (  # noqa: F401
+    attention_backward,
+    attention_backward_sampled,
+    attention_forward,
+    attention_forward_rows,
+    logits,
+    online_softmax_attention,
+    softmax_rows,
+    to_f64,
+    visible,
+)

@@ -1,0 +1,24 @@
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+    config.addinivalue_line("markers", "slow: CPU test that takes more than a few seconds")
+
+
+@pytest.fixture(scope="session")
+def gpu_lib():
+    """The HIP library through its Python binding; fails loudly if the GPU or library is missing."""
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("gpu test collected but no GPU is visible")
+    import exact_tiled_attention_06_amd as fa2
+    fa2.load_library()
+    return fa2

@@ -1,0 +1,113 @@
+"""Seeded synthetic inputs for the attention workloads.
+
+This module holds no attention arithmetic. It only draws inputs, so that the
+HIP path, the fp64 oracle, the tests and the benchmark all see the same bytes.
+
+Recipe (the same for every workload):
+  * ``torch.Generator('cpu').manual_seed(seed)``; ``randn`` in float32, drawn in
+    the order q, k, v, dout, each of shape ``[B, N, H, d]``;
+  * bf16 workloads round those float32 draws to bf16 (round-to-nearest-even,
+    ``Tensor.to(torch.bfloat16)``); both sides then read the same bf16 values;
+  * ALiBi slopes, when a workload uses them, are ``2**(-8*(h+1)/H)`` for head
+    ``h = 0..H-1``, stored as float32;
+  * the default input seed is the workload number (1..5) and the default
+    row-sampling seed is ``1000 + number``.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import numpy as np
+import torch
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    number: int
+    name: str
+    dtype: str          # "f32" or "bf16": element type of q, k, v, out, dout, dq, dk, dv
+    B: int
+    H: int
+    N: int
+    d: int
+    causal: bool
+    window: tuple       # (window_left, window_right); -1 = unbounded
+    alibi: bool
+    backward: bool      # whether the workload includes the backward pass
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+    @property
+    def torch_dtype(self):
+        return torch.float32 if self.dtype == "f32" else torch.bfloat16
+
+    def shape(self):
+        return (self.B, self.N, self.H, self.d)
+
+    def describe(self) -> str:
+        w = "" if self.window == (-1, -1) else f" window={self.window}"
+        return (f"{self.name}: {self.dtype} B={self.B} H={self.H} N={self.N} d={self.d}"
+                f" causal={int(self.causal)}{w} alibi={int(self.alibi)}")
+
+
+WORKLOADS = {
+    1: Workload(1, "tiny_f32_fwd", "f32", 1, 2, 128, 64, False, (-1, -1), False, False),
+    2: Workload(2, "bf16_fwd_n2048_d64", "bf16", 8, 16, 2048, 64, False, (-1, -1), False, False),
+    3: Workload(3, "bf16_causal_fwd_n8192_d128", "bf16", 4, 32, 8192, 128, True, (-1, -1), False, False),
+    4: Workload(4, "bf16_causal_bwd_n4096_d128", "bf16", 4, 16, 4096, 128, True, (-1, -1), False, True),
+    5: Workload(5, "bf16_window_alibi_n16384_d128", "bf16", 1, 32, 16384, 128, True, (4096, 0), True, True),
+}
+
+
+def alibi_slopes(H: int) -> torch.Tensor:
+    """ALiBi slopes 2**(-8*(h+1)/H), h = 0..H-1, as float32 (an input, not a computation step)."""
+    return torch.tensor([2.0 ** (-8.0 * (h + 1) / H) for h in range(H)], dtype=torch.float32)
+
+
+def make_inputs(B, H, N, d, dtype="bf16", seed=0, with_dout=False):
+    """Draw q, k, v (and dout) of shape [B, N, H, d] on the CPU, in the recipe above."""
+    g = torch.Generator(device="cpu").manual_seed(int(seed))
+    shape = (B, N, H, d)
+    names = ["q", "k", "v"] + (["dout"] if with_dout else [])
+    out = {}
+    for nm in names:
+        x = torch.randn(shape, generator=g, dtype=torch.float32)
+        out[nm] = x if dtype == "f32" else x.to(torch.bfloat16)
+    return out
+
+
+def workload_inputs(w: Workload, seed=None, with_dout=None):
+    """Inputs for a numbered workload, including ALiBi slopes (or None)."""
+    seed = w.number if seed is None else seed
+    with_dout = w.backward if with_dout is None else with_dout
+    t = make_inputs(w.B, w.H, w.N, w.d, w.dtype, seed, with_dout)
+    t["alibi_slopes"] = alibi_slopes(w.H) if w.alibi else None
+    return t
+
+
+def sample_query_rows(B, H, N, count=256, seed=0):
+    """`count` distinct (b, h, i) triples drawn uniformly with the seed, sorted."""
+    rng = np.random.default_rng(seed)
+    total = B * H * N
+    count = min(count, total)
+    flat = np.sort(rng.choice(total, size=count, replace=False))
+    b = flat // (H * N)
+    h = (flat // N) % H
+    i = flat % N
+    return np.stack([b, h, i], axis=1).astype(np.int64)
+
+
+def sample_key_rows(B, H, N, count=256, max_heads=4, seed=0):
+    """`count` distinct (b, h, j) key triples drawn from at most `max_heads` seeded heads."""
+    rng = np.random.default_rng(seed + 7919)
+    heads = rng.choice(B * H, size=min(max_heads, B * H), replace=False)
+    per = max(1, count // len(heads))
+    rows = []
+    for bh in np.sort(heads):
+        js = np.sort(rng.choice(N, size=min(per, N), replace=False))
+        for j in js:
+            rows.append((bh // H, bh % H, j))
+    return np.array(rows, dtype=np.int64)

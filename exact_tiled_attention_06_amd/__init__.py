@@ -1,0 +1,201 @@
+"""Python binding of libfa2.so, the MI355X exact-attention library.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in include/fa2.h. PyTorch supplies device
+memory and the current stream. If the library has not been built, every call
+raises FA2Error; there is no fallback path.
+
+Low-level functions carry the C names and arguments (fa2_fwd, fa2_fwd_f32,
+fa2_bwd, fa2_bwd_workspace_size, fa2_status_string, fa2_version); tensors or
+raw device addresses (int) are accepted for pointers. The convenience
+functions ``flash_attn_fwd`` / ``flash_attn_bwd`` mirror the parameter list of
+the FlashAttention v2 API on the wmrh.cn article (section 5.1) minus dropout:
+softmax_scale=None (-> 1/sqrt(d)), causal, window_size=(-1, -1), alibi_slopes,
+and deterministic for the backward.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+__all__ = [
+    "FA2Error", "LIB_PATH", "load_library", "fa2_fwd", "fa2_fwd_f32", "fa2_bwd",
+    "fa2_bwd_workspace_size", "fa2_status_string", "fa2_version", "flash_attn_fwd",
+    "flash_attn_bwd", "FA2_OK", "FA2_ERR_INVALID_ARG", "FA2_ERR_UNSUPPORTED", "FA2_ERR_HIP",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa2.so")
+
+FA2_OK = 0
+FA2_ERR_INVALID_ARG = 1
+FA2_ERR_UNSUPPORTED = 2
+FA2_ERR_HIP = 3
+
+_lib = None
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_F = ctypes.c_float
+
+# C signatures of include/fa2.h
+SIGNATURES = {
+    "fa2_fwd": ([_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _I, _I, _P, _P], _I),
+    "fa2_fwd_f32": ([_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _I, _I, _P, _P], _I),
+    "fa2_bwd_workspace_size": ([_I, _I, _I, _I], ctypes.c_size_t),
+    "fa2_bwd": ([_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _I, _I, _I, _I, _F, _I, _I, _I,
+                 _P, _I, _P], _I),
+    "fa2_status_string": ([_I], ctypes.c_char_p),
+    "fa2_version": ([], _I),
+}
+
+
+class FA2Error(RuntimeError):
+    def __init__(self, msg, status=None):
+        super().__init__(msg)
+        self.status = status
+
+
+def load_library(path: str | None = None):
+    """Load libfa2.so (once). Raises FA2Error if it has not been built."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise FA2Error(f"HIP library not built: {p} (run __graft_entry__.build())")
+    lib = ctypes.CDLL(p)
+    for name, (args, res) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(status: int, what: str):
+    if status != FA2_OK:
+        raise FA2Error(f"{what}: {fa2_status_string(status)}", status)
+
+
+def fa2_status_string(status: int) -> str:
+    s = load_library().fa2_status_string(int(status))
+    return s.decode() if s else "unknown"
+
+
+def fa2_version() -> int:
+    return int(load_library().fa2_version())
+
+
+def fa2_fwd(q, k, v, out, lse, B, H, N, d, softmax_scale, causal, window_left, window_right,
+            alibi_slopes=None, stream=None):
+    st = load_library().fa2_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), int(B), int(H), int(N),
+                                int(d), float(softmax_scale), int(causal), int(window_left),
+                                int(window_right), _ptr(alibi_slopes), _stream(stream))
+    _check(st, "fa2_fwd")
+
+
+def fa2_fwd_f32(q, k, v, out, lse, B, H, N, d, softmax_scale, causal, window_left, window_right,
+                alibi_slopes=None, stream=None):
+    st = load_library().fa2_fwd_f32(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), int(B), int(H),
+                                    int(N), int(d), float(softmax_scale), int(causal), int(window_left),
+                                    int(window_right), _ptr(alibi_slopes), _stream(stream))
+    _check(st, "fa2_fwd_f32")
+
+
+def fa2_bwd_workspace_size(B, H, N, d) -> int:
+    return int(load_library().fa2_bwd_workspace_size(int(B), int(H), int(N), int(d)))
+
+
+def fa2_bwd(q, k, v, out, lse, dout, dq, dk, dv, workspace, workspace_bytes, B, H, N, d, softmax_scale,
+            causal, window_left, window_right, alibi_slopes=None, deterministic=0, stream=None):
+    st = load_library().fa2_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dout), _ptr(dq),
+                                _ptr(dk), _ptr(dv), _ptr(workspace), int(workspace_bytes), int(B), int(H),
+                                int(N), int(d), float(softmax_scale), int(causal), int(window_left),
+                                int(window_right), _ptr(alibi_slopes), int(deterministic),
+                                _stream(stream))
+    _check(st, "fa2_bwd")
+
+
+# ------------------------------------------------------------------ convenience wrappers
+
+def _check_tensors(*ts):
+    import torch
+    ref = ts[0]
+    for t in ts:
+        if not isinstance(t, torch.Tensor):
+            raise FA2Error("expected torch tensors")
+        if not t.is_cuda or t.device != ref.device:
+            raise FA2Error("all tensors must be on the same GPU")
+        if not t.is_contiguous():
+            raise FA2Error("tensors must be contiguous [B, N, H, d]")
+        if t.dtype != ref.dtype or t.shape != ref.shape:
+            raise FA2Error("q, k, v (and out, dout) must share dtype and shape")
+
+
+def _slopes(alibi_slopes, H, device):
+    import torch
+    if alibi_slopes is None:
+        return None
+    s = alibi_slopes.to(device=device, dtype=torch.float32).contiguous()
+    if s.numel() != H:
+        raise FA2Error("alibi_slopes must have H entries")
+    return s
+
+
+def flash_attn_fwd(q, k, v, softmax_scale=None, causal=False, window_size=(-1, -1), alibi_slopes=None):
+    """Exact attention forward. q, k, v: [B, N, H, d] bf16 or float32 on the GPU.
+    Returns (out [B, N, H, d], lse [B, H, N] float32, natural log)."""
+    import torch
+    _check_tensors(q, k, v)
+    B, N, H, d = q.shape
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    out = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    sl = _slopes(alibi_slopes, H, q.device)
+    if q.dtype == torch.bfloat16:
+        fn = fa2_fwd
+    elif q.dtype == torch.float32:
+        fn = fa2_fwd_f32
+    else:
+        raise FA2Error(f"unsupported dtype {q.dtype}")
+    fn(q, k, v, out, lse, B, H, N, d, scale, int(bool(causal)), window_size[0], window_size[1], sl)
+    return out, lse
+
+
+def flash_attn_bwd(dout, q, k, v, out, lse, softmax_scale=None, causal=False, window_size=(-1, -1),
+                   alibi_slopes=None, deterministic=False, workspace=None):
+    """Exact attention backward from the forward's out and lse. bf16 [B, N, H, d] tensors.
+    Returns (dq, dk, dv)."""
+    import torch
+    _check_tensors(q, k, v, out, dout)
+    if q.dtype != torch.bfloat16:
+        raise FA2Error("the backward takes bf16 tensors")
+    B, N, H, d = q.shape
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    need = fa2_bwd_workspace_size(B, H, N, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    sl = _slopes(alibi_slopes, H, q.device)
+    fa2_bwd(q, k, v, out, lse, dout, dq, dk, dv, workspace, workspace.numel() * workspace.element_size(),
+            B, H, N, d, scale, int(bool(causal)), window_size[0], window_size[1], sl, int(bool(deterministic)))
+    return dq, dk, dv

@@ -1,0 +1,127 @@
+// Device helpers for the gfx950 attention kernels: vector types, MFMA and LDS
+// transpose-read wrappers, wavefront reductions and launch parameter blocks.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa2 {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+#define FA2_LDS __attribute__((address_space(3)))
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+// Finite stand-in for "no score seen yet" in the running max, so that
+// exp2(m_old - m_new) never evaluates (-inf) - (-inf).
+constexpr float kNoMax = -1.0e30f;
+
+// D = A * B + C on a 32x32x16 bf16 tile. Lane l supplies row (A) / column (B)
+// l % 32 and 8 consecutive reduction slots for half l / 32. C/D: lane l, reg r
+// holds row 8*(r/4) + 4*(l/32) + r%4, column l % 32.
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// 16-byte LDS read at a byte offset from the start of dynamic/static LDS.
+__device__ __forceinline__ bf16x8 lds_read16(const char* base, uint32_t off) {
+  return *reinterpret_cast<const bf16x8*>(base + off);
+}
+
+// ds_read_b64_tr_b16: inside each group of 16 lanes, lane i receives four
+// 16-bit values; value e comes from the 8 bytes addressed by group lane
+// 4*e + i/4, element i%4. If group lane j addresses row (r0 + j/4), columns
+// (c0 + 4*(j%4) .. +3) of a row-major matrix, lane i receives column c0 + i,
+// rows r0 .. r0+3: a 4x16 block read transposed.
+__device__ __forceinline__ bf16x4 lds_read_tr(const char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((bf16x4 FA2_LDS*)(p));
+}
+
+// Value of the lane 32 positions away (lane l <-> l ^ 32), via v_permlane32_swap.
+__device__ __forceinline__ float other_half(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  // lanes 0..31: r[0] = own, r[1] = partner; lanes 32..63: r[0] = partner, r[1] = own
+  return (threadIdx.x & 32) ? __uint_as_float(r[0]) : __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ float max_with_other_half(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float sum_with_other_half(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Eight fp32 values -> eight bf16 (round to nearest even; v_cvt_pk_bf16_f32).
+__device__ __forceinline__ bf16x8 pack_bf16x8(float a0, float a1, float a2, float a3, float a4,
+                                              float a5, float a6, float a7) {
+  bf16x8 r;
+  r[0] = (bf16)a0; r[1] = (bf16)a1; r[2] = (bf16)a2; r[3] = (bf16)a3;
+  r[4] = (bf16)a4; r[5] = (bf16)a5; r[6] = (bf16)a6; r[7] = (bf16)a7;
+  return r;
+}
+
+__device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
+
+// The key (within a 32-key subtile) that C register r of a lane in half hh
+// holds after S^T = K Q^T, when A-operand lane m loads key row kperm(m).
+// With kperm below, registers 0..7 of half hh are keys 8*hh + 0..7 and
+// registers 8..15 are keys 16 + 8*hh + 0..7: eight consecutive keys per
+// 16-key reduction step, the layout the P*V step consumes directly.
+__device__ __forceinline__ int kperm(int m) {
+  const int a = m >> 3, hh = (m >> 2) & 1, b = m & 3;
+  return 16 * (a >> 1) + 8 * hh + 4 * (a & 1) + b;
+}
+__host__ __device__ constexpr int key_of_reg(int r, int hh) { return 16 * (r >> 3) + 8 * hh + (r & 7); }
+
+struct FwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  const float* alibi;  // [H] or null
+  int B, H, N;
+  int n_qblocks;
+  float scale;       // softmax scale
+  float scale_log2;  // softmax scale * log2(e)
+  int causal;
+  int wl;            // window left (-1 = unbounded)
+  int wr;            // window right after the causal clamp (-1 = unbounded)
+};
+
+struct BwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const float* lse;
+  const void* dout;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* dq_acc;  // [B, H, N, d] float32 workspace
+  float* delta;   // [B, H, N] float32 workspace
+  const float* alibi;
+  int B, H, N;
+  float scale;
+  float scale_log2;
+  int causal;
+  int wl;
+  int wr;
+};
+
+}  // namespace fa2

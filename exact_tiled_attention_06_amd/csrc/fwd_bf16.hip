@@ -1,0 +1,300 @@
+// Forward attention, bf16 storage, on gfx950 MFMA.
+//
+// Method ("AI基础 | Flash Attention", sections Tiling分块 / 在线softmax /
+// Flash Attention2; FlashAttention-2 paper abstract, items (1)-(3)):
+// one workgroup per (batch, head, block of BR query rows); the K/V tiles of
+// the visible key range stream through LDS; every wavefront owns 32 query rows
+// and keeps its running max, running sum and unnormalised running output in
+// registers; the output is divided by the running sum once, at the end; only
+// O and the per-row logsumexp are written back.
+//
+// gfx950 mapping (the pages' kernel was written for NVIDIA parts):
+//  * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 with K as the A operand (from
+//    LDS) and Q^T as the B operand (registers, loaded once). Each lane then
+//    holds the scores of ONE query row (lane % 32) for 16 keys of a 32-key
+//    subtile, so the row max / row sum are in-lane plus a single
+//    v_permlane32_swap between the two lane halves.
+//  * O^T += V^T P^T with P^T as the B operand straight from registers (the K
+//    rows are loaded in a permuted order so that each lane half holds eight
+//    consecutive keys per 16-key reduction step), and V^T read from the
+//    row-major V tile with ds_read_b64_tr_b16. O^T keeps each query's
+//    accumulator in the same lanes as its softmax statistics, so the rescale by
+//    exp2(m_old - m_new) and the final 1/l are per-lane scalars.
+//  * The running max is kept in log2 units (scores times scale*log2 e) and
+//    the output is rescaled only when some row's max grew by more than
+//    2^kRescaleLog2 — every P then stays <= 2^kRescaleLog2 — which is exact:
+//    numerator and denominator share the same reference max.
+//  * K/V tiles: register-staged global loads for tile t+1 are issued before
+//    the MFMAs of tile t, written to the other half of a 2-stage LDS ring
+//    afterwards; one barrier per tile. LDS rows are XOR-swizzled in 16-byte
+//    chunks so that the 16-byte K reads and the transposed V reads are free of
+//    bank conflicts.
+//  * Causal / windowed grids run the longest query blocks first; masks are
+//    evaluated only on tiles that cross a mask edge or the end of the sequence.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace fa2 {
+
+constexpr float kRescaleLog2 = 8.0f;
+
+// 16-byte chunk position of chunk `cc` of row `r` in an LDS tile.
+template <int D>
+__device__ __forceinline__ int k_swz(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+template <int D>
+__device__ __forceinline__ int v_swz(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
+
+template <int D>
+__device__ __forceinline__ uint32_t k_off(int r, int cc) { return r * (D * 2) + ((cc ^ k_swz<D>(r)) << 4); }
+template <int D>
+__device__ __forceinline__ uint32_t v_off(int r, int cc) { return r * (D * 2) + ((cc ^ v_swz<D>(r)) << 4); }
+
+template <int D, int NW, int BC>
+struct FwdShape {
+  static constexpr int NT = NW * 64;        // threads
+  static constexpr int BR = NW * 32;        // query rows per workgroup
+  static constexpr int CPR = D / 8;         // 16-byte chunks per row
+  static constexpr int TILE = BC * D * 2;   // bytes of one K (or V) tile
+  static constexpr int CPT = BC * CPR / NT; // chunks per thread per tile
+  static constexpr int NSUB = BC / 32;      // 32-key subtiles per tile
+  static constexpr int KS = D / 16;         // MFMA reduction steps over d
+  static constexpr int MB = D / 32;         // 32-row blocks of O^T
+  static constexpr int LDS = 2 * 2 * TILE;  // two stages of K and V
+  static_assert((BC * CPR) % NT == 0, "tile must split evenly over threads");
+};
+
+template <int D, int NW, int BC, bool ALIBI>
+__global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdParams p) {
+  using S = FwdShape<D, NW, BC>;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+
+  const int bh_count = p.B * p.H;
+  const int qb = p.n_qblocks - 1 - (int)(blockIdx.x / bh_count);  // longest blocks first
+  const int bh = (int)(blockIdx.x % bh_count);
+  const int b = bh / p.H, h = bh % p.H;
+  const int N = p.N;
+
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
+  const int64_t rs = (int64_t)p.H * D;  // elements between consecutive tokens
+  const int64_t base = (int64_t)b * N * rs + (int64_t)h * D;
+  const bf16* qg = (const bf16*)p.q + base;
+  const bf16* kg = (const bf16*)p.k + base;
+  const bf16* vg = (const bf16*)p.v + base;
+  bf16* og = (bf16*)p.o + base;
+
+  const int q0 = qb * S::BR;
+  const int q_last = min(q0 + S::BR, N) - 1;
+  const int qw0 = q0 + 32 * w;        // first query row of this wave
+  const int qi = qw0 + l32;           // query row of this lane
+  const bool wave_live = qw0 < N;
+  const int wq_last = min(qw0 + 31, N - 1);
+
+  // Q^T fragments: lane holds q[qi][16*ks + 8*hh .. +7] for every step ks.
+  bf16x8 qf[S::KS];
+#pragma unroll
+  for (int ks = 0; ks < S::KS; ++ks) {
+    if (qi < N) {
+      qf[ks] = *reinterpret_cast<const bf16x8*>(qg + (int64_t)qi * rs + 16 * ks + 8 * hh);
+    } else {
+      qf[ks] = bf16x8{};
+    }
+  }
+
+  float slope2 = 0.f;
+  if (ALIBI) slope2 = p.alibi[h] * kLog2e;
+
+  // Visible key range of the whole block.
+  int kv_lo = 0, kv_hi = N;
+  if (p.wl >= 0) kv_lo = max(0, q0 - p.wl);
+  if (p.wr >= 0) kv_hi = min(N, q_last + p.wr + 1);
+  const int t_lo = kv_lo / BC, t_hi = (kv_hi + BC - 1) / BC;
+
+  f32x16 o[S::MB];
+#pragma unroll
+  for (int mb = 0; mb < S::MB; ++mb) o[mb] = f32x16{};
+  float m2 = kNoMax;  // running max, log2 units
+  float l = 0.f;      // running sum (this lane half's keys)
+
+  u32x4 kr[S::CPT], vr[S::CPT];
+  auto load_tile = [&](int t) {
+#pragma unroll
+    for (int i = 0; i < S::CPT; ++i) {
+      const int c = tid + i * S::NT;
+      const int r = c / S::CPR, cc = c % S::CPR;
+      const int key = t * BC + r;
+      if (key < N) {
+        kr[i] = *reinterpret_cast<const u32x4*>(kg + (int64_t)key * rs + cc * 8);
+        vr[i] = *reinterpret_cast<const u32x4*>(vg + (int64_t)key * rs + cc * 8);
+      } else {
+        kr[i] = u32x4{0, 0, 0, 0};
+        vr[i] = u32x4{0, 0, 0, 0};
+      }
+    }
+  };
+  auto store_tile = [&](int stage) {
+    char* kb = smem + stage * 2 * S::TILE;
+    char* vb = kb + S::TILE;
+#pragma unroll
+    for (int i = 0; i < S::CPT; ++i) {
+      const int c = tid + i * S::NT;
+      const int r = c / S::CPR, cc = c % S::CPR;
+      *reinterpret_cast<u32x4*>(kb + k_off<D>(r, cc)) = kr[i];
+      *reinterpret_cast<u32x4*>(vb + v_off<D>(r, cc)) = vr[i];
+    }
+  };
+
+  // One tile of the online softmax for this wave.
+  auto compute = [&](int stage, int j0, auto masked_tag) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
+    const char* kb = smem + stage * 2 * S::TILE;
+    const char* vb = kb + S::TILE;
+
+    // S^T = K Q^T for each 32-key subtile.
+    f32x16 s[S::NSUB];
+#pragma unroll
+    for (int sub = 0; sub < S::NSUB; ++sub) {
+      s[sub] = f32x16{};
+      const int krow = 32 * sub + kperm(l32);
+#pragma unroll
+      for (int ks = 0; ks < S::KS; ++ks) {
+        const bf16x8 a = lds_read16(kb, k_off<D>(krow, 2 * ks + hh));
+        s[sub] = mfma32(a, qf[ks], s[sub]);
+      }
+    }
+
+    // Mask, bias, row max.
+    float mx = -INFINITY;
+#pragma unroll
+    for (int sub = 0; sub < S::NSUB; ++sub) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float x = s[sub][r];
+        const int key = j0 + 32 * sub + key_of_reg(r, hh);
+        if (ALIBI) x = fmaf(x, p.scale_log2, -slope2 * fabsf((float)(qi - key)));
+        if (MASKED) {
+          const bool vis = key < N && (p.wr < 0 || key <= qi + p.wr) && (p.wl < 0 || key >= qi - p.wl);
+          x = vis ? x : -INFINITY;
+        }
+        s[sub][r] = x;
+        mx = fmaxf(mx, x);
+      }
+    }
+    if (!ALIBI) mx *= p.scale_log2;
+    mx = max_with_other_half(mx);
+
+    const float cand = fmaxf(m2, mx);
+    if (wave_any(cand - m2 > kRescaleLog2)) {
+      const float alpha = fast_exp2(m2 - cand);
+      m2 = cand;
+      l *= alpha;
+#pragma unroll
+      for (int mb = 0; mb < S::MB; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[mb][r] *= alpha;
+    }
+
+    // P = exp2(y - m2), running sum, then O^T += V^T P^T.
+    const int g = lane >> 4, j = lane & 15;
+#pragma unroll
+    for (int sub = 0; sub < S::NSUB; ++sub) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float pv = ALIBI ? fast_exp2(s[sub][r] - m2) : fast_exp2(fmaf(s[sub][r], p.scale_log2, -m2));
+        s[sub][r] = pv;
+        l += pv;
+      }
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const bf16x8 pb = pack_bf16x8(s[sub][8 * kk + 0], s[sub][8 * kk + 1], s[sub][8 * kk + 2],
+                                      s[sub][8 * kk + 3], s[sub][8 * kk + 4], s[sub][8 * kk + 5],
+                                      s[sub][8 * kk + 6], s[sub][8 * kk + 7]);
+        const int vrow = 32 * sub + 16 * kk + 8 * hh + (j >> 2);
+#pragma unroll
+        for (int mb = 0; mb < S::MB; ++mb) {
+          const int dcol = 32 * mb + 16 * (g & 1) + 4 * (j & 3);
+          const uint32_t in_chunk = (dcol & 7) * 2;
+          const bf16x4 lo = lds_read_tr(vb + v_off<D>(vrow, dcol >> 3) + in_chunk);
+          const bf16x4 hi = lds_read_tr(vb + v_off<D>(vrow + 4, dcol >> 3) + in_chunk);
+          const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          o[mb] = mfma32(a, pb, o[mb]);
+        }
+      }
+    }
+  };
+
+  load_tile(t_lo);
+  store_tile(0);
+  __syncthreads();
+  for (int t = t_lo; t < t_hi; ++t) {
+    const int stage = (t - t_lo) & 1;
+    const bool more = t + 1 < t_hi;
+    if (more) load_tile(t + 1);
+    const int j0 = t * BC;
+    const int j1 = j0 + BC - 1;
+    const bool skip = !wave_live || (p.wr >= 0 && j0 > wq_last + p.wr) || (p.wl >= 0 && j1 < qw0 - p.wl);
+    if (!skip) {
+      const bool full = j1 < N && (p.wr < 0 || j1 <= qw0 + p.wr) && (p.wl < 0 || j0 >= wq_last - p.wl);
+      if (full) {
+        compute(stage, j0, std::false_type{});
+      } else {
+        compute(stage, j0, std::true_type{});
+      }
+    }
+    if (more) store_tile(stage ^ 1);
+    __syncthreads();
+  }
+
+  if (!wave_live) return;
+  const float lt = sum_with_other_half(l);
+  const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+  if (qi < N) {
+    bf16* orow = og + (int64_t)qi * rs;
+#pragma unroll
+    for (int mb = 0; mb < S::MB; ++mb) {
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        bf16x4 val;
+        val[0] = (bf16)(o[mb][4 * a + 0] * inv);
+        val[1] = (bf16)(o[mb][4 * a + 1] * inv);
+        val[2] = (bf16)(o[mb][4 * a + 2] * inv);
+        val[3] = (bf16)(o[mb][4 * a + 3] * inv);
+        *reinterpret_cast<bf16x4*>(orow + 32 * mb + 8 * a + 4 * hh) = val;
+      }
+    }
+    if (hh == 0) p.lse[(int64_t)bh * N + qi] = lt > 0.f ? (m2 + log2f(lt)) * kLn2 : -INFINITY;
+  }
+}
+
+template <int D, int NW, int BC, bool ALIBI>
+static hipError_t launch_fwd_cfg(const FwdParams& p0, hipStream_t stream) {
+  using S = FwdShape<D, NW, BC>;
+  FwdParams p = p0;
+  p.n_qblocks = (p.N + S::BR - 1) / S::BR;
+  auto kern = fwd_bf16_kernel<D, NW, BC, ALIBI>;
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, S::LDS);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const int64_t nblk = (int64_t)p.n_qblocks * p.B * p.H;
+  hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3(S::NT), S::LDS, stream, p);
+  return hipGetLastError();
+}
+
+int64_t fwd_bf16_grid_blocks(int B, int H, int N, int d) {
+  (void)d;
+  const int BR = 4 * 32;
+  return (int64_t)((N + BR - 1) / BR) * B * H;
+}
+
+hipError_t launch_fwd_bf16(const FwdParams& p, int d, hipStream_t stream) {
+  const bool alibi = p.alibi != nullptr;
+  if (d == 128) {
+    return alibi ? launch_fwd_cfg<128, 4, 64, true>(p, stream) : launch_fwd_cfg<128, 4, 64, false>(p, stream);
+  }
+  return alibi ? launch_fwd_cfg<64, 4, 64, true>(p, stream) : launch_fwd_cfg<64, 4, 64, false>(p, stream);
+}
+
+}  // namespace fa2

@@ -1,0 +1,119 @@
+/*
+ * fa2.h -- C ABI of an MI355X (gfx950) exact-attention library in the
+ * FlashAttention-2 style: tiled, online softmax, the N x N score matrix never
+ * reaches HBM, the forward keeps one logsumexp per row and the backward
+ * recomputes the scores from it.
+ *
+ * What is computed (for every batch b, head h, query row i):
+ *   S_ij  = softmax_scale * <q_i, k_j> - slope_h * |i - j|      (key j visible)
+ *   S_ij  = -inf                                                 (key j masked)
+ *   LSE_i = ln sum_j exp(S_ij)
+ *   O_i   = sum_j exp(S_ij - LSE_i) v_j
+ * Sources: "AI基础 | Flash Attention" (sections on standard attention, tiling,
+ * online softmax and backward recomputation); the FlashAttention-2 paper
+ * abstract ("Faster Attention with Better Parallelism and Work Partitioning"):
+ * the result is exact, no approximation; the wmrh.cn FlashAttention v2 article,
+ * section 5.1 (API changes): softmax_scale, causal, window_size (-1 = unbounded)
+ * and alibi_slopes.
+ *
+ * Visibility of key j to query i (bounds inclusive):
+ *   (!causal || j <= i) && (window_left < 0 || j >= i - window_left)
+ *                       && (window_right' < 0 || j <= i + window_right'),
+ * where window_right' = 0 when causal, else window_right.
+ *
+ * Conventions shared by every entry point
+ *   - Layouts: q, k, v, out, dout, dq, dk, dv are contiguous [B, N, H, d]
+ *     (token-major, heads interleaved); lse is contiguous [B, H, N] float32
+ *     (natural log); alibi_slopes is [H] float32 or NULL (no bias).
+ *   - Memory: every pointer is DEVICE memory allocated and owned by the
+ *     caller. The library allocates nothing, frees nothing, keeps no state
+ *     between calls and is safe to call from several host threads.
+ *   - Streams: `stream` is a hipStream_t passed as void* (NULL = the default
+ *     stream). All work is queued on it and the call returns at once; a
+ *     kernel fault surfaces at the caller's next synchronisation.
+ *   - Errors: arguments are validated before any HIP call; on error nothing
+ *     is launched and the status says why. B, H or N equal to 0 is an empty
+ *     problem: FA2_OK, nothing launched, pointers not inspected.
+ *   - Alignment: every tensor pointer must be 16-byte aligned.
+ *   - Supported shapes: d in {64, 128}; any N >= 1 (ragged tails masked);
+ *     B * H <= 2^31 - 1; B * N * H * d < 2^62.
+ */
+#ifndef FA2_H
+#define FA2_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FA2_OK = 0,
+  FA2_ERR_INVALID_ARG = 1, /* null pointer, negative size, bad window, bad scale, misalignment */
+  FA2_ERR_UNSUPPORTED = 2, /* a valid request this build does not implement (e.g. d not in {64,128}) */
+  FA2_ERR_HIP = 3          /* the HIP runtime reported an error at launch */
+} fa2_status_t;
+
+/*
+ * Forward, bf16 storage, fp32 accumulation.
+ * q, k, v: bf16 [B, N, H, d] (read); out: bf16 [B, N, H, d] (written, O rounded
+ * to nearest even); lse: float32 [B, H, N] (written).
+ * softmax_scale must be finite and > 0 (the Python wrapper maps None to
+ * 1/sqrt(d)). window_left / window_right >= -1. causal != 0 means j <= i.
+ * Source: the online-softmax forward of "AI基础 | Flash Attention" (sections
+ * Tiling分块, 在线softmax, Flash Attention2) with the section 5.1 parameters of
+ * the wmrh.cn FlashAttention v2 article.
+ */
+fa2_status_t fa2_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
+                     int B, int H, int N, int d, float softmax_scale, int causal,
+                     int window_left, int window_right, const float* alibi_slopes,
+                     void* stream);
+
+/* Forward with float32 storage (q, k, v, out all float32); same arguments and
+ * semantics as fa2_fwd. P is kept in float32 (no bf16 rounding anywhere). */
+fa2_status_t fa2_fwd_f32(const float* q, const float* k, const float* v, float* out, float* lse,
+                         int B, int H, int N, int d, float softmax_scale, int causal,
+                         int window_left, int window_right, const float* alibi_slopes,
+                         void* stream);
+
+/*
+ * Bytes of device workspace fa2_bwd needs for this shape (a float32 dQ
+ * accumulator [B, H, N, d] and the per-row D = rowsum(dO * O) [B, H, N], each
+ * 256-byte aligned). Returns 0 for an empty or invalid shape.
+ */
+size_t fa2_bwd_workspace_size(int B, int H, int N, int d);
+
+/*
+ * Backward, bf16 storage. Gradients of sum(out * dout) with respect to q, k, v,
+ * recomputing the scores from q, k, v and the forward's lse (the recompute
+ * idea of "AI基础 | Flash Attention", section 反向传播):
+ *   P = exp(S - LSE), dV = P^T dO, dP = dO V^T, D = rowsum(dO * O),
+ *   dS = P * (dP - D), dQ = scale * dS K, dK = scale * dS^T Q.
+ * q, k, v, out, dout: bf16 [B, N, H, d] (read); lse: float32 [B, H, N] (read,
+ * as written by fa2_fwd with the same arguments); dq, dk, dv: bf16 [B, N, H, d]
+ * (written). workspace: device memory of at least fa2_bwd_workspace_size()
+ * bytes (workspace_bytes says how much was given; too little is
+ * FA2_ERR_INVALID_ARG); its contents need not be initialised and are
+ * overwritten. deterministic = 0: dQ is accumulated with float32 atomics, so
+ * dq may differ in the last bits between runs; deterministic != 0: dQ is
+ * computed by a separate pass without atomics and is bitwise repeatable.
+ * No gradient is produced for the ALiBi slopes.
+ */
+fa2_status_t fa2_bwd(const void* q, const void* k, const void* v, const void* out,
+                     const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                     void* workspace, size_t workspace_bytes,
+                     int B, int H, int N, int d, float softmax_scale, int causal,
+                     int window_left, int window_right, const float* alibi_slopes,
+                     int deterministic, void* stream);
+
+/* Static, human-readable name of a status code. */
+const char* fa2_status_string(fa2_status_t status);
+
+/* Library version as 10000*major + 100*minor + patch. */
+int fa2_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA2_H */

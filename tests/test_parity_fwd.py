@@ -1,0 +1,141 @@
+"""Forward parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Small shapes are compared element by element on every output; they span
+several 64-key tiles and 128-row query blocks and end in a ragged tail. The
+full-size workloads are compared on 256 seeded query rows plus fixed edge rows,
+in the same launch configuration the benchmark times.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from parity_utils import (TOL_LSE, TOL_O_BF16, TOL_O_F32, edge_rows, gather_lse, gather_rows,
+                          gpu_inputs, max_abs, oracle_forward_rows, say, scale_of, to_np)
+
+pytestmark = pytest.mark.gpu
+
+MASKS = {
+    "full": (False, (-1, -1), False),
+    "causal": (True, (-1, -1), False),
+    "window_37_5": (False, (37, 5), False),
+    "window_0_0": (False, (0, 0), False),
+    "causal_window_70": (True, (70, 0), False),
+    "causal_window_alibi": (True, (100, 0), True),
+    "alibi_noncausal": (False, (-1, -1), True),
+    "window_left_only": (False, (50, -1), False),
+}
+
+
+def run_fwd(fa2, dev, slopes, scale, causal, window):
+    sl = None if slopes is None else slopes.cuda()
+    out, lse = fa2.flash_attn_fwd(dev["q"], dev["k"], dev["v"], scale, causal, window, sl)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("mask", sorted(MASKS))
+def test_small_bf16_all_outputs(gpu_lib, d, mask):
+    causal, window, alibi = MASKS[mask]
+    B, H, N = 2, 3, 301  # 3 query blocks of 128 rows, 5 key tiles of 64, ragged tail
+    say(f"fwd bf16 small d={d} mask={mask} B={B} H={H} N={N}")
+    cpu, dev, slopes = gpu_inputs(B, H, N, d, "bf16", seed=11 + d, alibi=alibi)
+    out, lse = run_fwd(gpu_lib, dev, slopes, scale_of(d), causal, window)
+    o_ref, lse_ref = oracle.attention_forward(cpu["q"], cpu["k"], cpu["v"], scale_of(d), causal, window,
+                                              None if slopes is None else slopes.numpy())
+    eo, el = max_abs(to_np(out), o_ref), max_abs(to_np(lse), lse_ref)
+    say(f"  max|dO|={eo:.3e} max|dLSE|={el:.3e}")
+    assert eo <= TOL_O_BF16 and el <= TOL_LSE
+
+
+@pytest.mark.parametrize("N", [1, 2, 17, 63, 64, 65, 127, 128, 129, 200])
+@pytest.mark.parametrize("causal", [False, True])
+def test_edge_lengths(gpu_lib, N, causal):
+    say(f"fwd bf16 edge N={N} causal={causal}")
+    cpu, dev, _ = gpu_inputs(1, 2, N, 128, "bf16", seed=N)
+    out, lse = run_fwd(gpu_lib, dev, None, scale_of(128), causal, (-1, -1))
+    o_ref, lse_ref = oracle.attention_forward(cpu["q"], cpu["k"], cpu["v"], scale_of(128), causal)
+    assert max_abs(to_np(out), o_ref) <= TOL_O_BF16
+    assert max_abs(to_np(lse), lse_ref) <= TOL_LSE
+    if causal:
+        # causal row 0 is exactly V[0] and its LSE is scale * q0.k0
+        assert torch.equal(out[:, 0].cpu(), cpu["v"][:, 0])
+
+
+def test_single_key_returns_v(gpu_lib):
+    cpu, dev, _ = gpu_inputs(3, 4, 1, 64, "bf16", seed=5)
+    out, lse = run_fwd(gpu_lib, dev, None, 0.3, False, (-1, -1))
+    assert torch.equal(out.cpu(), cpu["v"])
+    ref = 0.3 * torch.einsum("bnhd,bnhd->bhn", cpu["q"].double(), cpu["k"].double())
+    assert max_abs(to_np(lse), ref.numpy()) <= TOL_LSE
+
+
+def test_constant_v(gpu_lib):
+    cpu, dev, _ = gpu_inputs(1, 2, 257, 128, "bf16", seed=6)
+    row = torch.linspace(-2, 2, 128).to(torch.bfloat16)
+    dev["v"] = row.expand(1, 257, 2, 128).contiguous().cuda()
+    out, _ = run_fwd(gpu_lib, dev, None, scale_of(128), True, (40, 0))
+    assert max_abs(to_np(out), row.float().expand(1, 257, 2, 128).numpy()) <= 1e-2
+
+
+def test_tiny_fp32_workload_full_check(gpu_lib):
+    w = workloads.WORKLOADS[1]
+    say(f"fwd {w.describe()}")
+    t = workloads.workload_inputs(w)
+    out, lse = run_fwd(gpu_lib, {k: t[k].cuda() for k in ("q", "k", "v")}, None, w.scale, w.causal, w.window)
+    o_ref, lse_ref = oracle.attention_forward(t["q"], t["k"], t["v"], w.scale, w.causal, w.window)
+    eo, el = max_abs(to_np(out), o_ref), max_abs(to_np(lse), lse_ref)
+    say(f"  max|dO|={eo:.3e} max|dLSE|={el:.3e}")
+    assert eo <= TOL_O_F32 and el <= TOL_O_F32
+
+
+@pytest.mark.parametrize("mask", ["full", "causal", "causal_window_alibi", "window_37_5"])
+def test_fp32_small_masks(gpu_lib, mask):
+    causal, window, alibi = MASKS[mask]
+    cpu, dev, slopes = gpu_inputs(2, 2, 150, 64, "f32", seed=9, alibi=alibi)
+    out, lse = run_fwd(gpu_lib, dev, slopes, 0.125, causal, window)
+    o_ref, lse_ref = oracle.attention_forward(cpu["q"], cpu["k"], cpu["v"], 0.125, causal, window,
+                                              None if slopes is None else slopes.numpy())
+    assert max_abs(to_np(out), o_ref) <= TOL_O_F32
+    assert max_abs(to_np(lse), lse_ref) <= TOL_O_F32
+
+
+@pytest.mark.parametrize("number", [2, 3, 4, 5])
+def test_full_size_workload_sampled_rows(gpu_lib, number):
+    w = workloads.WORKLOADS[number]
+    say(f"fwd full-size {w.describe()}")
+    t = workloads.workload_inputs(w, with_dout=False)
+    dev = {k: t[k].cuda() for k in ("q", "k", "v")}
+    out, lse = run_fwd(gpu_lib, dev, t["alibi_slopes"], w.scale, w.causal, w.window)
+    rows = workloads.sample_query_rows(w.B, w.H, w.N, 256, seed=1000 + number)
+    rows = np.concatenate([rows, edge_rows(w.B, w.H, w.N, extra=(1, 127, 128, w.window[0], w.window[0] + 1))])
+    o_ref, lse_ref = oracle_forward_rows(t, rows, w.scale, w.causal, w.window, t["alibi_slopes"])
+    o_np = out.float().cpu().numpy()
+    lse_np = lse.cpu().numpy()
+    eo = max_abs(gather_rows(o_np, rows), o_ref)
+    el = max_abs(gather_lse(lse_np, rows), lse_ref)
+    say(f"  rows={len(rows)} max|dO|={eo:.3e} max|dLSE|={el:.3e}")
+    assert eo <= TOL_O_BF16 and el <= TOL_LSE
+    assert np.isfinite(o_np).all() and np.isfinite(lse_np).all()
+
+
+def test_forward_is_bitwise_repeatable(gpu_lib):
+    cpu, dev, slopes = gpu_inputs(2, 4, 1000, 128, "bf16", seed=21, alibi=True)
+    o1, l1 = run_fwd(gpu_lib, dev, slopes, scale_of(128), True, (300, 0))
+    o2, l2 = run_fwd(gpu_lib, dev, slopes, scale_of(128), True, (300, 0))
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_explicit_stream(gpu_lib):
+    cpu, dev, _ = gpu_inputs(1, 2, 130, 64, "bf16", seed=3)
+    s = torch.cuda.Stream()
+    out = torch.empty_like(dev["q"])
+    lse = torch.empty((1, 2, 130), dtype=torch.float32, device="cuda")
+    with torch.cuda.stream(s):
+        gpu_lib.fa2_fwd(dev["q"], dev["k"], dev["v"], out, lse, 1, 2, 130, 64, 0.125, 0, -1, -1, None,
+                        s.cuda_stream)
+    s.synchronize()
+    o_ref, _ = oracle.attention_forward(cpu["q"], cpu["k"], cpu["v"], 0.125)
+    assert max_abs(to_np(out), o_ref) <= TOL_O_BF16

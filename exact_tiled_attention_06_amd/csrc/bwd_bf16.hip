@@ -1,7 +1,569 @@
-// Backward attention (placeholder until the MFMA backward lands).
+// Backward attention, bf16 storage, on gfx950 MFMA.
+//
+// Method ("AI基础 | Flash Attention", section 反向传播): the forward kept one
+// softmax statistic per row (here the logsumexp LSE); the backward rebuilds
+// P = exp(S - LSE) tile by tile from Q, K and the statistic, on chip, and never
+// writes an N x N matrix. The gradient formulas are the chain rule on the
+// definition:  dV = P^T dO,  dP = dO V^T,  D = rowsum(dO * O),
+// dS = P * (dP - D),  dQ = scale * dS K,  dK = scale * dS^T Q.
+//
+// Passes (one stream, in order):
+//  1. bwd_pre_kernel: D = rowsum(dO * O) in float32; zeroes the float32 dQ
+//     accumulator when dQ is accumulated atomically.
+//  2. bwd_main_kernel: one workgroup per (batch, head, block of 128 keys) —
+//     the parallelisation over blocks within one head of the FlashAttention-2
+//     paper abstract, item (2), applied to the key axis. Every wavefront owns
+//     32 keys and keeps its dK^T and dV^T accumulators in registers while the
+//     visible 32-query blocks stream through a 2-stage LDS ring.
+//     S = Q K^T and dP = dO V^T are computed with queries on the MFMA rows and
+//     the wave's keys on the columns, so P and dS come out of the C registers
+//     with eight consecutive queries per lane half: exactly the B operand of
+//     dV^T += dO^T P and dK^T += Q^T dS; dO^T and Q^T are read transposed from
+//     LDS with ds_read_b64_tr_b16. dS^T goes through LDS once so that each
+//     wave can form a 32 x 32 block of dQ = dS K over all 128 keys of the
+//     workgroup, added to the float32 accumulator with global float atomics.
+//  3. bwd_dq_convert_kernel: dQ = scale * accumulator, rounded to bf16.
+// Deterministic variant: pass 2 skips dQ, and bwd_dq_det_kernel forms dQ per
+// 128-query block by a key sweep shaped like the forward (S^T = K Q^T,
+// dP^T = V dO^T, dQ^T += K^T dS^T), with no atomics.
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace fa2 {
-hipError_t launch_bwd_bf16(const BwdParams&, int, bool, hipStream_t) { return hipErrorNotSupported; }
+
+template <int D>
+struct BwdShape {
+  static constexpr int NW = 4;
+  static constexpr int NT = NW * 64;
+  static constexpr int BK = NW * 32;                    // keys per workgroup
+  static constexpr int BQ = 32;                         // queries per iteration
+  static constexpr int CPR = D / 8;                     // 16-byte chunks per row
+  static constexpr int KS = D / 16;                     // MFMA steps over d
+  static constexpr int MB = D / 32;                     // 32-row blocks of d
+  static constexpr int K_BYTES = BK * D * 2;            // resident K tile
+  static constexpr int QT_BYTES = BQ * D * 2;           // one Q or dO tile
+  static constexpr int STAGE_BYTES = 2 * QT_BYTES + 2 * BQ * 4;
+  static constexpr int DS_BYTES = BK * BQ * 2;          // dS^T, [key][query]
+  static constexpr int LDS = K_BYTES + 2 * STAGE_BYTES + DS_BYTES;
+  static constexpr int QCPT = BQ * CPR / NT;            // Q chunks per thread
+  static constexpr int KCPT = BK * CPR / NT;            // K chunks per thread
+  static constexpr int DQ_SPLIT = NW / MB;              // waves per d-block in the dQ step
+  static_assert(BQ * CPR % NT == 0 && BK * CPR % NT == 0, "even split");
+};
+
+// dS^T tile: rows of 32 queries (64 bytes); chunk c of key row r at c ^ ((r/4)%4).
+__device__ __forceinline__ uint32_t ds_off(int r, int c) { return r * 64 + ((c ^ ((r >> 2) & 3)) << 4); }
+__device__ __forceinline__ uint32_t ds_off_tr(int r, int col) { return ds_off(r, col >> 3) + (col & 7) * 2; }
+
+// ---------------------------------------------------------------- pass 1
+template <int D>
+__global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p, int zero_acc) {
+  constexpr int CPR = D / 8;
+  constexpr int RPB = 256 / CPR;
+  const int64_t total = (int64_t)p.B * p.N * p.H;
+  const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / CPR;  // token-major (b, i, h)
+  const int cc = threadIdx.x % CPR;
+  float acc = 0.f;
+  if (row < total) {
+    const bf16x8 o = *reinterpret_cast<const bf16x8*>((const bf16*)p.o + row * D + cc * 8);
+    const bf16x8 g = *reinterpret_cast<const bf16x8*>((const bf16*)p.dout + row * D + cc * 8);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc = fmaf((float)o[e], (float)g[e], acc);
+  }
+#pragma unroll
+  for (int off = CPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+  if (row < total) {
+    const int64_t h = row % p.H;
+    const int64_t i = (row / p.H) % p.N;
+    const int64_t b = row / ((int64_t)p.H * p.N);
+    const int64_t bhrow = (b * p.H + h) * p.N + i;
+    if (cc == 0) p.delta[bhrow] = acc;
+    if (zero_acc) {
+      f32x4* dst = reinterpret_cast<f32x4*>(p.dq_acc + bhrow * D + cc * 8);
+      dst[0] = f32x4{0.f, 0.f, 0.f, 0.f};
+      dst[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+}
+
+// ---------------------------------------------------------------- pass 3
+template <int D>
+__global__ __launch_bounds__(256) void bwd_dq_convert_kernel(BwdParams p) {
+  constexpr int CPR = D / 8;
+  constexpr int RPB = 256 / CPR;
+  const int64_t total = (int64_t)p.B * p.N * p.H;
+  const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / CPR;
+  const int cc = threadIdx.x % CPR;
+  if (row >= total) return;
+  const int64_t h = row % p.H;
+  const int64_t i = (row / p.H) % p.N;
+  const int64_t b = row / ((int64_t)p.H * p.N);
+  const int64_t bhrow = (b * p.H + h) * p.N + i;
+  const f32x4* src = reinterpret_cast<const f32x4*>(p.dq_acc + bhrow * D + cc * 8);
+  const f32x4 x0 = src[0], x1 = src[1];
+  const float s = p.scale;
+  *reinterpret_cast<bf16x8*>((bf16*)p.dq + row * D + cc * 8) =
+      pack_bf16x8(x0[0] * s, x0[1] * s, x0[2] * s, x0[3] * s, x1[0] * s, x1[1] * s, x1[2] * s, x1[3] * s);
+}
+
+// ---------------------------------------------------------------- pass 2
+template <int D, bool ALIBI, bool DET>
+__global__ __launch_bounds__(256, 1) void bwd_main_kernel(BwdParams p) {
+  using S = BwdShape<D>;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  char* k_lds = smem;
+  char* stage_lds = smem + S::K_BYTES;
+  char* ds_lds = stage_lds + 2 * S::STAGE_BYTES;
+
+  const int bh_count = p.B * p.H;
+  const int kb = (int)(blockIdx.x / bh_count);  // low key blocks see the most queries: first
+  const int bh = (int)(blockIdx.x % bh_count);
+  const int b = bh / p.H, h = bh % p.H;
+  const int N = p.N;
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
+  const int g = lane >> 4, j = lane & 15;
+  const int64_t rs = (int64_t)p.H * D;
+  const int64_t base = (int64_t)b * N * rs + (int64_t)h * D;
+  const bf16* qg = (const bf16*)p.q + base;
+  const bf16* kg = (const bf16*)p.k + base;
+  const bf16* vg = (const bf16*)p.v + base;
+  const bf16* dog = (const bf16*)p.dout + base;
+  const float* lse_g = p.lse + (int64_t)bh * N;
+  const float* del_g = p.delta + (int64_t)bh * N;
+
+  const int k0 = kb * S::BK;
+  const int k_last = min(k0 + S::BK, N) - 1;
+  const int kw0 = k0 + 32 * w;  // first key of this wave
+  const int kj = kw0 + l32;     // key of this lane (MFMA column)
+
+  // V^T fragments (B operand of dP = dO V^T): lane holds v[kj][16*ks + 8*hh .. +7].
+  bf16x8 vf[S::KS];
+#pragma unroll
+  for (int ks = 0; ks < S::KS; ++ks)
+    vf[ks] = kj < N ? *reinterpret_cast<const bf16x8*>(vg + (int64_t)kj * rs + 16 * ks + 8 * hh) : bf16x8{};
+  // Resident K tile in LDS (B operand of S, and K of dQ = dS K).
+#pragma unroll
+  for (int i = 0; i < S::KCPT; ++i) {
+    const int c = tid + i * S::NT;
+    const int r = c / S::CPR, cc = c % S::CPR;
+    const int key = k0 + r;
+    const u32x4 x = key < N ? *reinterpret_cast<const u32x4*>(kg + (int64_t)key * rs + cc * 8) : u32x4{0, 0, 0, 0};
+    *reinterpret_cast<u32x4*>(k_lds + tile_off<D>(r, cc)) = x;
+  }
+
+  const float slope2 = ALIBI ? p.alibi[h] * kLog2e : 0.f;
+
+  // Query blocks that can see any key of this workgroup.
+  int q_lo = 0, q_hi = N - 1;
+  if (p.wr >= 0) q_lo = max(0, k0 - p.wr);
+  if (p.wl >= 0) q_hi = min(N - 1, k_last + p.wl);
+  const int it_lo = q_lo / S::BQ, it_hi = q_hi / S::BQ + 1;
+
+  f32x16 dk[S::MB], dv[S::MB];
+#pragma unroll
+  for (int mb = 0; mb < S::MB; ++mb) {
+    dk[mb] = f32x16{};
+    dv[mb] = f32x16{};
+  }
+
+  u32x4 qs[S::QCPT], os[S::QCPT];
+  float ls = 0.f;
+  auto load_q = [&](int it) {
+    const int i0 = it * S::BQ;
+#pragma unroll
+    for (int i = 0; i < S::QCPT; ++i) {
+      const int c = tid + i * S::NT;
+      const int r = c / S::CPR, cc = c % S::CPR;
+      const int q = i0 + r;
+      if (q < N) {
+        qs[i] = *reinterpret_cast<const u32x4*>(qg + (int64_t)q * rs + cc * 8);
+        os[i] = *reinterpret_cast<const u32x4*>(dog + (int64_t)q * rs + cc * 8);
+      } else {
+        qs[i] = u32x4{0, 0, 0, 0};
+        os[i] = u32x4{0, 0, 0, 0};
+      }
+    }
+    if (tid < S::BQ) {
+      const int q = i0 + tid;
+      ls = q < N ? lse_g[q] * kLog2e : INFINITY;  // rows past the end get P = 0
+    } else if (tid < 2 * S::BQ) {
+      const int q = i0 + tid - S::BQ;
+      ls = q < N ? del_g[q] : 0.f;
+    }
+  };
+  auto store_q = [&](int stage) {
+    char* st = stage_lds + stage * S::STAGE_BYTES;
+#pragma unroll
+    for (int i = 0; i < S::QCPT; ++i) {
+      const int c = tid + i * S::NT;
+      const int r = c / S::CPR, cc = c % S::CPR;
+      *reinterpret_cast<u32x4*>(st + tile_off<D>(r, cc)) = qs[i];
+      *reinterpret_cast<u32x4*>(st + S::QT_BYTES + tile_off<D>(r, cc)) = os[i];
+    }
+    if (tid < 2 * S::BQ) reinterpret_cast<float*>(st + 2 * S::QT_BYTES)[tid] = ls;
+  };
+
+  auto compute = [&](int stage, int i0, auto masked_tag) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
+    const char* q_t = stage_lds + stage * S::STAGE_BYTES;
+    const char* do_t = q_t + S::QT_BYTES;
+    const float* lse2_t = reinterpret_cast<const float*>(q_t + 2 * S::QT_BYTES);
+    const float* del_t = lse2_t + S::BQ;
+
+    // S = Q K^T and dP = dO V^T: rows are queries (A lane m reads row kperm(m)), columns are keys.
+    f32x16 s = f32x16{}, dp = f32x16{};
+    const int arow = kperm(l32);
+#pragma unroll
+    for (int ks = 0; ks < S::KS; ++ks) {
+      const bf16x8 a = lds_read16(q_t, tile_off<D>(arow, 2 * ks + hh));
+      const bf16x8 bk = lds_read16(k_lds, tile_off<D>(32 * w + l32, 2 * ks + hh));
+      s = mfma32(a, bk, s);
+      const bf16x8 ao = lds_read16(do_t, tile_off<D>(arow, 2 * ks + hh));
+      dp = mfma32(ao, vf[ks], dp);
+    }
+
+    // P = exp2(S*scale*log2e + bias - LSE*log2e); dS = P * (dP - D).
+    float pr[16], dsr[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int qr = key_of_reg(r, hh);  // query row within the block held by register r
+      const int q = i0 + qr;
+      float y = s[r] * p.scale_log2;
+      if (ALIBI) y = fmaf(-slope2, fabsf((float)(q - kj)), y);
+      float pv = fast_exp2(y - lse2_t[qr]);
+      if (MASKED) {
+        const bool vis = q < N && kj < N && (p.wr < 0 || kj <= q + p.wr) && (p.wl < 0 || kj >= q - p.wl);
+        pv = vis ? pv : 0.f;
+      }
+      pr[r] = pv;
+      dsr[r] = pv * (dp[r] - del_t[qr]);
+    }
+    bf16x8 pb[2], dsb[2];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      pb[kk] = pack_bf16x8(pr[8 * kk], pr[8 * kk + 1], pr[8 * kk + 2], pr[8 * kk + 3], pr[8 * kk + 4],
+                           pr[8 * kk + 5], pr[8 * kk + 6], pr[8 * kk + 7]);
+      dsb[kk] = pack_bf16x8(dsr[8 * kk], dsr[8 * kk + 1], dsr[8 * kk + 2], dsr[8 * kk + 3], dsr[8 * kk + 4],
+                            dsr[8 * kk + 5], dsr[8 * kk + 6], dsr[8 * kk + 7]);
+    }
+
+    // dV^T += dO^T P and dK^T += Q^T dS (A operands read transposed from LDS).
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int row = 16 * kk + 8 * hh + (j >> 2);
+#pragma unroll
+      for (int mb = 0; mb < S::MB; ++mb) {
+        const int col = 32 * mb + 16 * (g & 1) + 4 * (j & 3);
+        const bf16x4 o_lo = lds_read_tr(do_t + tile_off_tr<D>(row, col));
+        const bf16x4 o_hi = lds_read_tr(do_t + tile_off_tr<D>(row + 4, col));
+        const bf16x8 ao = {o_lo[0], o_lo[1], o_lo[2], o_lo[3], o_hi[0], o_hi[1], o_hi[2], o_hi[3]};
+        dv[mb] = mfma32(ao, pb[kk], dv[mb]);
+        const bf16x4 q_lo = lds_read_tr(q_t + tile_off_tr<D>(row, col));
+        const bf16x4 q_hi = lds_read_tr(q_t + tile_off_tr<D>(row + 4, col));
+        const bf16x8 aq = {q_lo[0], q_lo[1], q_lo[2], q_lo[3], q_hi[0], q_hi[1], q_hi[2], q_hi[3]};
+        dk[mb] = mfma32(aq, dsb[kk], dk[mb]);
+      }
+    }
+    if (!DET) {
+      const int row = 32 * w + l32;  // key row of dS^T
+      *reinterpret_cast<bf16x8*>(ds_lds + ds_off(row, hh)) = dsb[0];
+      *reinterpret_cast<bf16x8*>(ds_lds + ds_off(row, 2 + hh)) = dsb[1];
+    }
+  };
+
+  load_q(it_lo);
+  store_q(0);
+  __syncthreads();
+  for (int it = it_lo; it < it_hi; ++it) {
+    const int stage = (it - it_lo) & 1;
+    const bool more = it + 1 < it_hi;
+    if (more) load_q(it + 1);
+    const int i0 = it * S::BQ;
+    const int i1 = i0 + S::BQ - 1;
+    const bool skip = kw0 >= N || (p.wr >= 0 && i1 + p.wr < kw0) || (p.wl >= 0 && i0 - p.wl > kw0 + 31);
+    if (!skip) {
+      const bool full = i1 < N && kw0 + 31 < N && (p.wr < 0 || i0 + p.wr >= kw0 + 31) &&
+                        (p.wl < 0 || i1 - p.wl <= kw0);
+      if (full) {
+        compute(stage, i0, std::false_type{});
+      } else {
+        compute(stage, i0, std::true_type{});
+      }
+    } else if (!DET) {
+      const int row = 32 * w + l32;
+      *reinterpret_cast<u32x4*>(ds_lds + ds_off(row, hh)) = u32x4{0, 0, 0, 0};
+      *reinterpret_cast<u32x4*>(ds_lds + ds_off(row, 2 + hh)) = u32x4{0, 0, 0, 0};
+    }
+    if (!DET) {
+      __syncthreads();  // dS^T of all waves is in LDS
+      // dQ block: rows i0..i0+31, d columns 32*mbq .. +31, over this wave's share of the keys.
+      const int mbq = w % S::MB, part = w / S::MB;
+      constexpr int KSPAN = S::BK / S::DQ_SPLIT;
+      f32x16 dqa = f32x16{};
+#pragma unroll
+      for (int kk = 0; kk < KSPAN / 16; ++kk) {
+        const int krow = part * KSPAN + 16 * kk + 8 * hh + (j >> 2);
+        const int qcol = 16 * (g & 1) + 4 * (j & 3);
+        const bf16x4 a_lo = lds_read_tr(ds_lds + ds_off_tr(krow, qcol));
+        const bf16x4 a_hi = lds_read_tr(ds_lds + ds_off_tr(krow + 4, qcol));
+        const int dcol = 32 * mbq + 16 * (g & 1) + 4 * (j & 3);
+        const bf16x4 b_lo = lds_read_tr(k_lds + tile_off_tr<D>(krow, dcol));
+        const bf16x4 b_hi = lds_read_tr(k_lds + tile_off_tr<D>(krow + 4, dcol));
+        const bf16x8 a = {a_lo[0], a_lo[1], a_lo[2], a_lo[3], a_hi[0], a_hi[1], a_hi[2], a_hi[3]};
+        const bf16x8 bb = {b_lo[0], b_lo[1], b_lo[2], b_lo[3], b_hi[0], b_hi[1], b_hi[2], b_hi[3]};
+        dqa = mfma32(a, bb, dqa);
+      }
+      float* dq_row = p.dq_acc + ((int64_t)bh * N + i0) * D + 32 * mbq + l32;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = 8 * (r >> 2) + 4 * hh + (r & 3);
+        if (i0 + m < N) atomicAdd(dq_row + (int64_t)m * D, dqa[r]);
+      }
+    }
+    if (more) store_q(stage ^ 1);
+    __syncthreads();
+  }
+
+  // dK = scale * dK^T, dV = dV^T, stored as bf16: lane holds key kj, d = 32*mb + 8*a + 4*hh + (0..3).
+  if (kj < N) {
+    bf16* dk_row = (bf16*)p.dk + base + (int64_t)kj * rs;
+    bf16* dv_row = (bf16*)p.dv + base + (int64_t)kj * rs;
+#pragma unroll
+    for (int mb = 0; mb < S::MB; ++mb) {
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        bf16x4 xk, xv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          xk[e] = (bf16)(dk[mb][4 * a + e] * p.scale);
+          xv[e] = (bf16)(dv[mb][4 * a + e]);
+        }
+        *reinterpret_cast<bf16x4*>(dk_row + 32 * mb + 8 * a + 4 * hh) = xk;
+        *reinterpret_cast<bf16x4*>(dv_row + 32 * mb + 8 * a + 4 * hh) = xv;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- deterministic dQ
+template <int D, bool ALIBI>
+__global__ __launch_bounds__(256, 2) void bwd_dq_det_kernel(BwdParams p) {
+  constexpr int NW = 4, NT = 256, BR = NW * 32, BC = 32;
+  constexpr int CPR = D / 8, KS = D / 16, MB = D / 32;
+  constexpr int TILE = BC * D * 2;
+  constexpr int CPT = BC * CPR / NT;
+  static_assert(BC * CPR % NT == 0, "even split");
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+
+  const int bh_count = p.B * p.H;
+  const int n_qblocks = (p.N + BR - 1) / BR;
+  const int qb = n_qblocks - 1 - (int)(blockIdx.x / bh_count);
+  const int bh = (int)(blockIdx.x % bh_count);
+  const int b = bh / p.H, h = bh % p.H;
+  const int N = p.N;
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
+  const int g = lane >> 4, j = lane & 15;
+  const int64_t rs = (int64_t)p.H * D;
+  const int64_t base = (int64_t)b * N * rs + (int64_t)h * D;
+  const bf16* qg = (const bf16*)p.q + base;
+  const bf16* kg = (const bf16*)p.k + base;
+  const bf16* vg = (const bf16*)p.v + base;
+  const bf16* dog = (const bf16*)p.dout + base;
+
+  const int q0 = qb * BR;
+  const int q_last = min(q0 + BR, N) - 1;
+  const int qw0 = q0 + 32 * w;
+  const int qi = qw0 + l32;
+  const bool wave_live = qw0 < N;
+  const int wq_last = min(qw0 + 31, N - 1);
+
+  bf16x8 qf[KS], of[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    if (qi < N) {
+      qf[ks] = *reinterpret_cast<const bf16x8*>(qg + (int64_t)qi * rs + 16 * ks + 8 * hh);
+      of[ks] = *reinterpret_cast<const bf16x8*>(dog + (int64_t)qi * rs + 16 * ks + 8 * hh);
+    } else {
+      qf[ks] = bf16x8{};
+      of[ks] = bf16x8{};
+    }
+  }
+  const float lse2 = qi < N ? p.lse[(int64_t)bh * N + qi] * kLog2e : INFINITY;
+  const float delta = qi < N ? p.delta[(int64_t)bh * N + qi] : 0.f;
+  const float slope2 = ALIBI ? p.alibi[h] * kLog2e : 0.f;
+
+  int kv_lo = 0, kv_hi = N;
+  if (p.wl >= 0) kv_lo = max(0, q0 - p.wl);
+  if (p.wr >= 0) kv_hi = min(N, q_last + p.wr + 1);
+  const int t_lo = kv_lo / BC, t_hi = (kv_hi + BC - 1) / BC;
+
+  f32x16 acc[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) acc[mb] = f32x16{};
+
+  u32x4 kr[CPT], vr[CPT];
+  auto load_tile = [&](int t) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int c = tid + i * NT;
+      const int r = c / CPR, cc = c % CPR;
+      const int key = t * BC + r;
+      if (key < N) {
+        kr[i] = *reinterpret_cast<const u32x4*>(kg + (int64_t)key * rs + cc * 8);
+        vr[i] = *reinterpret_cast<const u32x4*>(vg + (int64_t)key * rs + cc * 8);
+      } else {
+        kr[i] = u32x4{0, 0, 0, 0};
+        vr[i] = u32x4{0, 0, 0, 0};
+      }
+    }
+  };
+  auto store_tile = [&](int stage) {
+    char* kb = smem + stage * 2 * TILE;
+    char* vb = kb + TILE;
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int c = tid + i * NT;
+      const int r = c / CPR, cc = c % CPR;
+      *reinterpret_cast<u32x4*>(kb + tile_off<D>(r, cc)) = kr[i];
+      *reinterpret_cast<u32x4*>(vb + tile_off<D>(r, cc)) = vr[i];
+    }
+  };
+
+  auto compute = [&](int stage, int j0, auto masked_tag) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
+    const char* kb = smem + stage * 2 * TILE;
+    const char* vb = kb + TILE;
+    // S^T = K Q^T and dP^T = V dO^T: rows are keys (A lane m reads row kperm(m)), columns queries.
+    f32x16 s = f32x16{}, dp = f32x16{};
+    const int arow = kperm(l32);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const bf16x8 ak = lds_read16(kb, tile_off<D>(arow, 2 * ks + hh));
+      s = mfma32(ak, qf[ks], s);
+      const bf16x8 av = lds_read16(vb, tile_off<D>(arow, 2 * ks + hh));
+      dp = mfma32(av, of[ks], dp);
+    }
+    float dsr[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = j0 + key_of_reg(r, hh);
+      float y = s[r] * p.scale_log2;
+      if (ALIBI) y = fmaf(-slope2, fabsf((float)(qi - key)), y);
+      float pv = fast_exp2(y - lse2);
+      if (MASKED) {
+        const bool vis = key < N && qi < N && (p.wr < 0 || key <= qi + p.wr) && (p.wl < 0 || key >= qi - p.wl);
+        pv = vis ? pv : 0.f;
+      }
+      dsr[r] = pv * (dp[r] - delta);
+    }
+    // dQ^T += K^T dS^T: A = K^T read transposed from the K tile, B = dS^T from registers.
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const bf16x8 dsb = pack_bf16x8(dsr[8 * kk], dsr[8 * kk + 1], dsr[8 * kk + 2], dsr[8 * kk + 3],
+                                     dsr[8 * kk + 4], dsr[8 * kk + 5], dsr[8 * kk + 6], dsr[8 * kk + 7]);
+      const int row = 16 * kk + 8 * hh + (j >> 2);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const int col = 32 * mb + 16 * (g & 1) + 4 * (j & 3);
+        const bf16x4 lo = lds_read_tr(kb + tile_off_tr<D>(row, col));
+        const bf16x4 hi = lds_read_tr(kb + tile_off_tr<D>(row + 4, col));
+        const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        acc[mb] = mfma32(a, dsb, acc[mb]);
+      }
+    }
+  };
+
+  load_tile(t_lo);
+  store_tile(0);
+  __syncthreads();
+  for (int t = t_lo; t < t_hi; ++t) {
+    const int stage = (t - t_lo) & 1;
+    const bool more = t + 1 < t_hi;
+    if (more) load_tile(t + 1);
+    const int j0 = t * BC, j1 = j0 + BC - 1;
+    const bool skip = !wave_live || (p.wr >= 0 && j0 > wq_last + p.wr) || (p.wl >= 0 && j1 < qw0 - p.wl);
+    if (!skip) {
+      const bool full = j1 < N && wq_last == qw0 + 31 && (p.wr < 0 || j1 <= qw0 + p.wr) &&
+                        (p.wl < 0 || j0 >= wq_last - p.wl);
+      if (full) {
+        compute(stage, j0, std::false_type{});
+      } else {
+        compute(stage, j0, std::true_type{});
+      }
+    }
+    if (more) store_tile(stage ^ 1);
+    __syncthreads();
+  }
+  if (!wave_live || qi >= N) return;
+  bf16* dq_row = (bf16*)p.dq + base + (int64_t)qi * rs;
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      bf16x4 x;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[e] = (bf16)(acc[mb][4 * a + e] * p.scale);
+      *reinterpret_cast<bf16x4*>(dq_row + 32 * mb + 8 * a + 4 * hh) = x;
+    }
+  }
+}
+
+// ---------------------------------------------------------------- launch
+template <typename K>
+static hipError_t set_lds(K kern, int bytes) {
+  return hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+}
+
+template <int D, bool ALIBI, bool DET>
+static hipError_t launch_bwd_cfg(const BwdParams& p, hipStream_t stream) {
+  using S = BwdShape<D>;
+  const int64_t rows = (int64_t)p.B * p.N * p.H;
+  constexpr int RPB = 256 / (D / 8);
+  const unsigned row_blocks = (unsigned)((rows + RPB - 1) / RPB);
+  hipLaunchKernelGGL(bwd_pre_kernel<D>, dim3(row_blocks), dim3(256), 0, stream, p, DET ? 0 : 1);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+
+  auto kmain = bwd_main_kernel<D, ALIBI, DET>;
+  static bool main_attr = false;
+  if (!main_attr) {
+    if ((e = set_lds(kmain, S::LDS)) != hipSuccess) return e;
+    main_attr = true;
+  }
+  const int nkb = (p.N + S::BK - 1) / S::BK;
+  hipLaunchKernelGGL(kmain, dim3((unsigned)((int64_t)nkb * p.B * p.H)), dim3(S::NT), S::LDS, stream, p);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+
+  if (DET) {
+    auto kdq = bwd_dq_det_kernel<D, ALIBI>;
+    constexpr int DQ_LDS = 2 * 2 * 32 * D * 2;
+    static bool dq_attr = false;
+    if (!dq_attr) {
+      if ((e = set_lds(kdq, DQ_LDS)) != hipSuccess) return e;
+      dq_attr = true;
+    }
+    const int nqb = (p.N + 127) / 128;
+    hipLaunchKernelGGL(kdq, dim3((unsigned)((int64_t)nqb * p.B * p.H)), dim3(256), DQ_LDS, stream, p);
+  } else {
+    hipLaunchKernelGGL(bwd_dq_convert_kernel<D>, dim3(row_blocks), dim3(256), 0, stream, p);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_bf16(const BwdParams& p, int d, bool deterministic, hipStream_t stream) {
+  const bool alibi = p.alibi != nullptr;
+  if (d == 128) {
+    if (deterministic)
+      return alibi ? launch_bwd_cfg<128, true, true>(p, stream) : launch_bwd_cfg<128, false, true>(p, stream);
+    return alibi ? launch_bwd_cfg<128, true, false>(p, stream) : launch_bwd_cfg<128, false, false>(p, stream);
+  }
+  if (deterministic)
+    return alibi ? launch_bwd_cfg<64, true, true>(p, stream) : launch_bwd_cfg<64, false, true>(p, stream);
+  return alibi ? launch_bwd_cfg<64, true, false>(p, stream) : launch_bwd_cfg<64, false, false>(p, stream);
+}
+
 }  // namespace fa2

@@ -87,6 +87,29 @@ __device__ __forceinline__ int kperm(int m) {
 }
 __host__ __device__ constexpr int key_of_reg(int r, int hh) { return 16 * (r >> 3) + 8 * hh + (r & 7); }
 
+// XOR swizzle of 16-byte chunks in an LDS tile of rows of D bf16 values.
+// It keeps two access patterns free of bank conflicts (64 banks x 4 bytes):
+//  * 16-byte row reads: 16 lanes read the same chunk of 16 consecutive rows;
+//  * transposed reads (ds_read_b64_tr_b16): 32 lanes read 4 consecutive rows
+//    (first row a multiple of 4) x 4 consecutive chunks.
+// D = 128 (16 chunks per 256-byte row): chunk c of row r sits at c ^ f(r),
+// f(r) = 4*(r%4) + (r/4)%4, a bijection on 16 consecutive rows whose high
+// part separates the 4 rows of a transposed read.
+// D = 64 (8 chunks, two rows per 256 bytes): f(r) = 4*((r/2)%2) + (r/4)%4.
+template <int D>
+__device__ __forceinline__ int tile_swz(int r) {
+  return D == 128 ? (4 * (r & 3) + ((r >> 2) & 3)) : (4 * ((r >> 1) & 1) + ((r >> 2) & 3));
+}
+template <int D>
+__device__ __forceinline__ uint32_t tile_off(int r, int cc) {
+  return r * (D * 2) + ((cc ^ tile_swz<D>(r)) << 4);
+}
+// Byte address of the 8-byte piece (row r, columns col..col+3) for a transposed read.
+template <int D>
+__device__ __forceinline__ uint32_t tile_off_tr(int r, int col) {
+  return tile_off<D>(r, col >> 3) + (col & 7) * 2;
+}
+
 struct FwdParams {
   const void* q;
   const void* k;

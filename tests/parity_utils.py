@@ -31,10 +31,13 @@ def max_abs(a, b):
     return float(np.max(np.abs(np.asarray(a, dtype=np.float64) - np.asarray(b, dtype=np.float64)))) if np.size(a) else 0.0
 
 
-def rel_to_max(a, ref):
+def rel_to_max(a, ref, floor=1e-3):
+    """max |a - ref| / max |ref|. The denominator is floored so that a reference
+    that is exactly zero by the mathematics (e.g. dQ and dK when every query sees
+    only itself, where dS = 0) turns into an absolute check."""
     ref = np.asarray(ref, dtype=np.float64)
     denom = float(np.max(np.abs(ref))) if ref.size else 0.0
-    return max_abs(a, ref) / max(denom, 1e-30)
+    return max_abs(a, ref) / max(denom, floor)
 
 
 def to_np(t):

@@ -1,0 +1,110 @@
+"""Backward parity: HIP gradients (through the C ABI) against the fp64 oracle.
+
+The forward's own O and LSE (from the HIP path) feed the HIP backward, as in
+use; the oracle recomputes everything from q, k, v, dout by the definition.
+Metric: max |error| / max |reference| per tensor <= 5e-2.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from parity_utils import TOL_GRAD_REL, edge_rows, gpu_inputs, rel_to_max, say, scale_of, to_np
+
+pytestmark = pytest.mark.gpu
+
+MASKS = {
+    "full": (False, (-1, -1), False),
+    "causal": (True, (-1, -1), False),
+    "window_37_5": (False, (37, 5), False),
+    "causal_window_70": (True, (70, 0), False),
+    "causal_window_alibi": (True, (100, 0), True),
+    "alibi_noncausal": (False, (-1, -1), True),
+    "window_0_0": (False, (0, 0), False),
+}
+
+
+def run_fwd_bwd(fa2, dev, slopes, scale, causal, window, deterministic=False):
+    sl = None if slopes is None else slopes.cuda()
+    out, lse = fa2.flash_attn_fwd(dev["q"], dev["k"], dev["v"], scale, causal, window, sl)
+    dq, dk, dv = fa2.flash_attn_bwd(dev["dout"], dev["q"], dev["k"], dev["v"], out, lse, scale, causal, window,
+                                    sl, deterministic)
+    torch.cuda.synchronize()
+    return dq, dk, dv
+
+
+def check_small(fa2, B, H, N, d, causal, window, alibi, deterministic, seed):
+    cpu, dev, slopes = gpu_inputs(B, H, N, d, "bf16", seed=seed, with_dout=True, alibi=alibi)
+    dq, dk, dv = run_fwd_bwd(fa2, dev, slopes, scale_of(d), causal, window, deterministic)
+    gq, gk, gv = oracle.attention_backward(cpu["q"], cpu["k"], cpu["v"], cpu["dout"], scale_of(d), causal, window,
+                                           None if slopes is None else slopes.numpy())
+    errs = [rel_to_max(to_np(x), r) for x, r in ((dq, gq), (dk, gk), (dv, gv))]
+    say(f"  rel-to-max err dq={errs[0]:.3e} dk={errs[1]:.3e} dv={errs[2]:.3e}")
+    assert max(errs) <= TOL_GRAD_REL, errs
+    return dq, dk, dv
+
+
+@pytest.mark.parametrize("deterministic", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("mask", sorted(MASKS))
+def test_small_bf16_gradients(gpu_lib, d, mask, deterministic):
+    causal, window, alibi = MASKS[mask]
+    say(f"bwd bf16 small d={d} mask={mask} det={deterministic}")
+    check_small(gpu_lib, 2, 3, 301, d, causal, window, alibi, deterministic, seed=31 + d)
+
+
+@pytest.mark.parametrize("N", [1, 17, 128, 129, 200])
+def test_edge_lengths(gpu_lib, N):
+    say(f"bwd bf16 edge N={N}")
+    check_small(gpu_lib, 1, 2, N, 128, True, (-1, -1), False, False, seed=N + 100)
+
+
+@pytest.mark.parametrize("deterministic", [False, True])
+def test_self_only_window_has_zero_dq_dk(gpu_lib, deterministic):
+    """window (0, 0): each query sees only itself, P = 1, D = dP, so dS = 0: dQ = dK = 0 and dV = dO."""
+    cpu, dev, _ = gpu_inputs(1, 2, 190, 128, "bf16", seed=43, with_dout=True)
+    dq, dk, dv = run_fwd_bwd(gpu_lib, dev, None, scale_of(128), False, (0, 0), deterministic)
+    assert float(dq.abs().max()) < 1e-4 and float(dk.abs().max()) < 1e-4
+    assert torch.equal(dv.cpu(), cpu["dout"])
+
+
+def test_deterministic_mode_is_bitwise_repeatable(gpu_lib):
+    cpu, dev, slopes = gpu_inputs(1, 4, 700, 128, "bf16", seed=41, with_dout=True, alibi=True)
+    a = run_fwd_bwd(gpu_lib, dev, slopes, scale_of(128), True, (200, 0), deterministic=True)
+    b = run_fwd_bwd(gpu_lib, dev, slopes, scale_of(128), True, (200, 0), deterministic=True)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+def test_dv_columns_sum_to_dout_columns(gpu_lib):
+    """Rows of P sum to 1, so sum_j dV_j = sum_i dO_i for every head (a property at any size)."""
+    cpu, dev, _ = gpu_inputs(2, 2, 513, 64, "bf16", seed=42, with_dout=True)
+    _, _, dv = run_fwd_bwd(gpu_lib, dev, None, scale_of(64), True, (-1, -1))
+    lhs = dv.double().sum(1).cpu().numpy()
+    rhs = cpu["dout"].double().sum(1).numpy()
+    assert np.max(np.abs(lhs - rhs)) / np.max(np.abs(rhs)) < 2e-2
+
+
+@pytest.mark.parametrize("deterministic", [False, True])
+@pytest.mark.parametrize("number", [4, 5])
+def test_full_size_workload_sampled_rows(gpu_lib, number, deterministic):
+    w = workloads.WORKLOADS[number]
+    say(f"bwd full-size {w.describe()} det={deterministic}")
+    t = workloads.workload_inputs(w, with_dout=True)
+    dev = {k: t[k].cuda() for k in ("q", "k", "v", "dout")}
+    dq, dk, dv = run_fwd_bwd(gpu_lib, dev, t["alibi_slopes"], w.scale, w.causal, w.window, deterministic)
+    qrows = workloads.sample_query_rows(w.B, w.H, w.N, 256, seed=1000 + number)
+    qrows = np.concatenate([qrows, edge_rows(w.B, w.H, w.N, extra=(1, 128, w.window[0]))])
+    krows = workloads.sample_key_rows(w.B, w.H, w.N, 256, max_heads=2, seed=1000 + number)
+    sl = None if t["alibi_slopes"] is None else t["alibi_slopes"].numpy()
+    gq, gk, gv = oracle.attention_backward_sampled(t["q"], t["k"], t["v"], t["dout"], qrows, krows, w.scale,
+                                                   w.causal, w.window, sl)
+    dq_np, dk_np, dv_np = (x.float().cpu().numpy() for x in (dq, dk, dv))
+    e_q = rel_to_max(dq_np[qrows[:, 0], qrows[:, 2], qrows[:, 1]], gq)
+    e_k = rel_to_max(dk_np[krows[:, 0], krows[:, 2], krows[:, 1]], gk)
+    e_v = rel_to_max(dv_np[krows[:, 0], krows[:, 2], krows[:, 1]], gv)
+    say(f"  rel-to-max err dq={e_q:.3e} dk={e_k:.3e} dv={e_v:.3e}")
+    assert max(e_q, e_k, e_v) <= TOL_GRAD_REL
+    for x in (dq_np, dk_np, dv_np):
+        assert np.isfinite(x).all()

@@ -110,8 +110,9 @@ __global__ __launch_bounds__(256) void bwd_dq_convert_kernel(BwdParams p) {
 
 // ---------------------------------------------------------------- pass 2
 template <int D, bool ALIBI, bool DET>
-__global__ __launch_bounds__(256, 1) void bwd_main_kernel(BwdParams p) {
+__global__ __launch_bounds__(256, D == 128 ? 1 : 2) void bwd_main_kernel(BwdParams p) {
   using S = BwdShape<D>;
+  constexpr int ROWB = 2 * D;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   char* k_lds = smem;
   char* stage_lds = smem + S::K_BYTES;
@@ -144,15 +145,8 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(BwdParams p) {
 #pragma unroll
   for (int ks = 0; ks < S::KS; ++ks)
     vf[ks] = kj < N ? *reinterpret_cast<const bf16x8*>(vg + (int64_t)kj * rs + 16 * ks + 8 * hh) : bf16x8{};
-  // Resident K tile in LDS (B operand of S, and K of dQ = dS K).
-#pragma unroll
-  for (int i = 0; i < S::KCPT; ++i) {
-    const int c = tid + i * S::NT;
-    const int r = c / S::CPR, cc = c % S::CPR;
-    const int key = k0 + r;
-    const u32x4 x = key < N ? *reinterpret_cast<const u32x4*>(kg + (int64_t)key * rs + cc * 8) : u32x4{0, 0, 0, 0};
-    *reinterpret_cast<u32x4*>(k_lds + tile_off<D>(r, cc)) = x;
-  }
+  // Resident K tile (B operand of S, and K of dQ = dS K).
+  dma_tile<D, S::BK, S::NW>(k_lds, kg, rs, k0, N, w, lane);
 
   const float slope2 = ALIBI ? p.alibi[h] * kLog2e : 0.f;
 
@@ -162,6 +156,24 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(BwdParams p) {
   if (p.wl >= 0) q_hi = min(N - 1, k_last + p.wl);
   const int it_lo = q_lo / S::BQ, it_hi = q_hi / S::BQ + 1;
 
+  // Per-lane LDS bases; every read below is base ^ constant or base + constant.
+  const int ar = kperm(l32);  // A-operand row (query) for S and dP
+  uint32_t qa_base = ar * ROWB + ((hh ^ tile_swz<D>(ar)) << 4);
+  uint32_t kb_base = (32 * w + l32) * ROWB + ((hh ^ tile_swz<D>(l32)) << 4);
+  const int tr0 = 8 * hh + (j >> 2);
+  const int c0 = 2 * (g & 1) + ((j & 3) >> 1);
+  uint32_t tr_lo = tr0 * ROWB + ((c0 ^ tile_swz<D>(tr0)) << 4) + (j & 1) * 8;
+  uint32_t tr_hi = (tr0 + 4) * ROWB + ((c0 ^ tile_swz<D>(tr0 + 4)) << 4) + (j & 1) * 8;
+  // dQ step: dS^T rows / K rows part*KSPAN + 8*hh + j/4 (+4) (+16*kk).
+  const int mbq = w % S::MB, part = w / S::MB;
+  constexpr int KSPAN = S::BK / S::DQ_SPLIT;
+  const int dr0 = part * KSPAN + tr0;
+  uint32_t ds_lo = dr0 * 64 + ((c0 ^ ((dr0 >> 2) & 3)) << 4) + (j & 1) * 8;
+  uint32_t ds_hi = (dr0 + 4) * 64 + ((c0 ^ (((dr0 + 4) >> 2) & 3)) << 4) + (j & 1) * 8;
+  const int kc0 = 4 * mbq + c0;  // K chunk for the dQ B operand
+  uint32_t kt_lo = dr0 * ROWB + ((kc0 ^ tile_swz<D>(dr0)) << 4) + (j & 1) * 8;
+  uint32_t kt_hi = (dr0 + 4) * ROWB + ((kc0 ^ tile_swz<D>(dr0 + 4)) << 4) + (j & 1) * 8;
+
   f32x16 dk[S::MB], dv[S::MB];
 #pragma unroll
   for (int mb = 0; mb < S::MB; ++mb) {
@@ -169,118 +181,102 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(BwdParams p) {
     dv[mb] = f32x16{};
   }
 
-  u32x4 qs[S::QCPT], os[S::QCPT];
-  float ls = 0.f;
-  auto load_q = [&](int it) {
-    const int i0 = it * S::BQ;
-#pragma unroll
-    for (int i = 0; i < S::QCPT; ++i) {
-      const int c = tid + i * S::NT;
-      const int r = c / S::CPR, cc = c % S::CPR;
-      const int q = i0 + r;
-      if (q < N) {
-        qs[i] = *reinterpret_cast<const u32x4*>(qg + (int64_t)q * rs + cc * 8);
-        os[i] = *reinterpret_cast<const u32x4*>(dog + (int64_t)q * rs + cc * 8);
-      } else {
-        qs[i] = u32x4{0, 0, 0, 0};
-        os[i] = u32x4{0, 0, 0, 0};
-      }
-    }
-    if (tid < S::BQ) {
-      const int q = i0 + tid;
-      ls = q < N ? lse_g[q] * kLog2e : INFINITY;  // rows past the end get P = 0
-    } else if (tid < 2 * S::BQ) {
-      const int q = i0 + tid - S::BQ;
-      ls = q < N ? del_g[q] : 0.f;
-    }
-  };
-  auto store_q = [&](int stage) {
+  // Q, dO (swizzled tiles) and LSE, D (raw floats) of query block `it` into a stage.
+  auto issue_q = [&](int it, int stage) {
     char* st = stage_lds + stage * S::STAGE_BYTES;
-#pragma unroll
-    for (int i = 0; i < S::QCPT; ++i) {
-      const int c = tid + i * S::NT;
-      const int r = c / S::CPR, cc = c % S::CPR;
-      *reinterpret_cast<u32x4*>(st + tile_off<D>(r, cc)) = qs[i];
-      *reinterpret_cast<u32x4*>(st + S::QT_BYTES + tile_off<D>(r, cc)) = os[i];
+    const int i0 = it * S::BQ;
+    dma_tile<D, S::BQ, S::NW>(st, qg, rs, i0, N, w, lane);
+    dma_tile<D, S::BQ, S::NW>(st + S::QT_BYTES, dog, rs, i0, N, w, lane);
+    if (w == 0) {
+      const int q = min(i0 + l32, N - 1);
+      const float* src = hh ? del_g + q : lse_g + q;
+      __builtin_amdgcn_global_load_lds((const void FA2_GLOBAL*)src, (void FA2_LDS*)(st + 2 * S::QT_BYTES), 4, 0, 0);
     }
-    if (tid < 2 * S::BQ) reinterpret_cast<float*>(st + 2 * S::QT_BYTES)[tid] = ls;
   };
 
   auto compute = [&](int stage, int i0, auto masked_tag) {
     constexpr bool MASKED = decltype(masked_tag)::value;
     const char* q_t = stage_lds + stage * S::STAGE_BYTES;
     const char* do_t = q_t + S::QT_BYTES;
-    const float* lse2_t = reinterpret_cast<const float*>(q_t + 2 * S::QT_BYTES);
-    const float* del_t = lse2_t + S::BQ;
+    const float* lse_t = reinterpret_cast<const float*>(q_t + 2 * S::QT_BYTES);
+    const float* del_t = lse_t + S::BQ;
 
-    // S = Q K^T and dP = dO V^T: rows are queries (A lane m reads row kperm(m)), columns are keys.
-    f32x16 s = f32x16{}, dp = f32x16{};
-    const int arow = kperm(l32);
+    // S = Q K^T: rows are queries (A lane m reads row kperm(m)), columns are this wave's keys.
+    f32x16 s = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < S::KS; ++ks) {
-      const bf16x8 a = lds_read16(q_t, tile_off<D>(arow, 2 * ks + hh));
-      const bf16x8 bk = lds_read16(k_lds, tile_off<D>(32 * w + l32, 2 * ks + hh));
+      const bf16x8 a = lds_read16(q_t, qa_base ^ (ks << 5));
+      const bf16x8 bk = lds_read16(k_lds, kb_base ^ (ks << 5));
       s = mfma32(a, bk, s);
-      const bf16x8 ao = lds_read16(do_t, tile_off<D>(arow, 2 * ks + hh));
-      dp = mfma32(ao, vf[ks], dp);
     }
-
-    // P = exp2(S*scale*log2e + bias - LSE*log2e); dS = P * (dP - D).
-    float pr[16], dsr[16];
+    // P = exp2(S*scale*log2e + bias - LSE*log2e), zero where masked.
+    float pr[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int qr = key_of_reg(r, hh);  // query row within the block held by register r
       const int q = i0 + qr;
       float y = s[r] * p.scale_log2;
       if (ALIBI) y = fmaf(-slope2, fabsf((float)(q - kj)), y);
-      float pv = fast_exp2(y - lse2_t[qr]);
+      float pv = fast_exp2(fmaf(lse_t[qr], -kLog2e, y));
       if (MASKED) {
         const bool vis = q < N && kj < N && (p.wr < 0 || kj <= q + p.wr) && (p.wl < 0 || kj >= q - p.wl);
         pv = vis ? pv : 0.f;
       }
       pr[r] = pv;
-      dsr[r] = pv * (dp[r] - del_t[qr]);
+    }
+    // dP = dO V^T, then dS = P * (dP - D).
+    f32x16 dp = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < S::KS; ++ks) {
+      const bf16x8 ao = lds_read16(do_t, qa_base ^ (ks << 5));
+      dp = mfma32(ao, vf[ks], dp);
     }
     bf16x8 pb[2], dsb[2];
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
+      float d8[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int r = 8 * kk + e;
+        d8[e] = pr[r] * (dp[r] - del_t[key_of_reg(r, hh)]);
+      }
       pb[kk] = pack_bf16x8(pr[8 * kk], pr[8 * kk + 1], pr[8 * kk + 2], pr[8 * kk + 3], pr[8 * kk + 4],
                            pr[8 * kk + 5], pr[8 * kk + 6], pr[8 * kk + 7]);
-      dsb[kk] = pack_bf16x8(dsr[8 * kk], dsr[8 * kk + 1], dsr[8 * kk + 2], dsr[8 * kk + 3], dsr[8 * kk + 4],
-                            dsr[8 * kk + 5], dsr[8 * kk + 6], dsr[8 * kk + 7]);
+      dsb[kk] = pack_bf16x8(d8[0], d8[1], d8[2], d8[3], d8[4], d8[5], d8[6], d8[7]);
     }
-
+    if (!DET) {
+      const int row = 32 * w + l32;  // key row of dS^T; chunk c holds queries 8c .. 8c+7
+      *reinterpret_cast<bf16x8*>(ds_lds + ds_off(row, hh)) = dsb[0];
+      *reinterpret_cast<bf16x8*>(ds_lds + ds_off(row, 2 + hh)) = dsb[1];
+    }
     // dV^T += dO^T P and dK^T += Q^T dS (A operands read transposed from LDS).
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-      const int row = 16 * kk + 8 * hh + (j >> 2);
 #pragma unroll
       for (int mb = 0; mb < S::MB; ++mb) {
-        const int col = 32 * mb + 16 * (g & 1) + 4 * (j & 3);
-        const bf16x4 o_lo = lds_read_tr(do_t + tile_off_tr<D>(row, col));
-        const bf16x4 o_hi = lds_read_tr(do_t + tile_off_tr<D>(row + 4, col));
+        const uint32_t x = (mb << 6) | (kk * 16 * ROWB);
+        const bf16x4 o_lo = lds_read_tr(do_t + (tr_lo ^ x));
+        const bf16x4 o_hi = lds_read_tr(do_t + (tr_hi ^ x));
         const bf16x8 ao = {o_lo[0], o_lo[1], o_lo[2], o_lo[3], o_hi[0], o_hi[1], o_hi[2], o_hi[3]};
         dv[mb] = mfma32(ao, pb[kk], dv[mb]);
-        const bf16x4 q_lo = lds_read_tr(q_t + tile_off_tr<D>(row, col));
-        const bf16x4 q_hi = lds_read_tr(q_t + tile_off_tr<D>(row + 4, col));
+        const bf16x4 q_lo = lds_read_tr(q_t + (tr_lo ^ x));
+        const bf16x4 q_hi = lds_read_tr(q_t + (tr_hi ^ x));
         const bf16x8 aq = {q_lo[0], q_lo[1], q_lo[2], q_lo[3], q_hi[0], q_hi[1], q_hi[2], q_hi[3]};
         dk[mb] = mfma32(aq, dsb[kk], dk[mb]);
       }
     }
-    if (!DET) {
-      const int row = 32 * w + l32;  // key row of dS^T
-      *reinterpret_cast<bf16x8*>(ds_lds + ds_off(row, hh)) = dsb[0];
-      *reinterpret_cast<bf16x8*>(ds_lds + ds_off(row, 2 + hh)) = dsb[1];
-    }
   };
 
-  load_q(it_lo);
-  store_q(0);
-  __syncthreads();
+  issue_q(it_lo, 0);
+  wait_all_and_sync();
   for (int it = it_lo; it < it_hi; ++it) {
     const int stage = (it - it_lo) & 1;
     const bool more = it + 1 < it_hi;
-    if (more) load_q(it + 1);
+    if (more) issue_q(it + 1, stage ^ 1);
+    opaque(qa_base);
+    opaque(kb_base);
+    opaque(tr_lo);
+    opaque(tr_hi);
     const int i0 = it * S::BQ;
     const int i1 = i0 + S::BQ - 1;
     const bool skip = kw0 >= N || (p.wr >= 0 && i1 + p.wr < kw0) || (p.wl >= 0 && i0 - p.wl > kw0 + 31);
@@ -299,19 +295,18 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(BwdParams p) {
     }
     if (!DET) {
       __syncthreads();  // dS^T of all waves is in LDS
+      opaque(ds_lo);
+      opaque(ds_hi);
+      opaque(kt_lo);
+      opaque(kt_hi);
       // dQ block: rows i0..i0+31, d columns 32*mbq .. +31, over this wave's share of the keys.
-      const int mbq = w % S::MB, part = w / S::MB;
-      constexpr int KSPAN = S::BK / S::DQ_SPLIT;
       f32x16 dqa = f32x16{};
 #pragma unroll
       for (int kk = 0; kk < KSPAN / 16; ++kk) {
-        const int krow = part * KSPAN + 16 * kk + 8 * hh + (j >> 2);
-        const int qcol = 16 * (g & 1) + 4 * (j & 3);
-        const bf16x4 a_lo = lds_read_tr(ds_lds + ds_off_tr(krow, qcol));
-        const bf16x4 a_hi = lds_read_tr(ds_lds + ds_off_tr(krow + 4, qcol));
-        const int dcol = 32 * mbq + 16 * (g & 1) + 4 * (j & 3);
-        const bf16x4 b_lo = lds_read_tr(k_lds + tile_off_tr<D>(krow, dcol));
-        const bf16x4 b_hi = lds_read_tr(k_lds + tile_off_tr<D>(krow + 4, dcol));
+        const bf16x4 a_lo = lds_read_tr(ds_lds + ds_lo + kk * 16 * 64);
+        const bf16x4 a_hi = lds_read_tr(ds_lds + ds_hi + kk * 16 * 64);
+        const bf16x4 b_lo = lds_read_tr(k_lds + kt_lo + kk * 16 * ROWB);
+        const bf16x4 b_hi = lds_read_tr(k_lds + kt_hi + kk * 16 * ROWB);
         const bf16x8 a = {a_lo[0], a_lo[1], a_lo[2], a_lo[3], a_hi[0], a_hi[1], a_hi[2], a_hi[3]};
         const bf16x8 bb = {b_lo[0], b_lo[1], b_lo[2], b_lo[3], b_hi[0], b_hi[1], b_hi[2], b_hi[3]};
         dqa = mfma32(a, bb, dqa);
@@ -323,8 +318,7 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(BwdParams p) {
         if (i0 + m < N) atomicAdd(dq_row + (int64_t)m * D, dqa[r]);
       }
     }
-    if (more) store_q(stage ^ 1);
-    __syncthreads();
+    wait_all_and_sync();
   }
 
   // dK = scale * dK^T, dV = dV^T, stored as bf16: lane holds key kj, d = 32*mb + 8*a + 4*hh + (0..3).
@@ -350,7 +344,7 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(BwdParams p) {
 
 // ---------------------------------------------------------------- deterministic dQ
 template <int D, bool ALIBI>
-__global__ __launch_bounds__(256, 2) void bwd_dq_det_kernel(BwdParams p) {
+__global__ __launch_bounds__(256, D == 128 ? 1 : 2) void bwd_dq_det_kernel(BwdParams p) {
   constexpr int NW = 4, NT = 256, BR = NW * 32, BC = 32;
   constexpr int CPR = D / 8, KS = D / 16, MB = D / 32;
   constexpr int TILE = BC * D * 2;

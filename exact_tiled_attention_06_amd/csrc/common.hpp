@@ -18,6 +18,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 #define FA2_LDS __attribute__((address_space(3)))
+#define FA2_GLOBAL __attribute__((address_space(1)))
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -108,6 +109,47 @@ __device__ __forceinline__ uint32_t tile_off(int r, int cc) {
 template <int D>
 __device__ __forceinline__ uint32_t tile_off_tr(int r, int col) {
   return tile_off<D>(r, col >> 3) + (col & 7) * 2;
+}
+
+// Copies rows [row0, row0 + ROWS) of one head (row stride rs elements) into
+// an LDS tile laid out with tile_off, using gfx950's direct global->LDS loads
+// (global_load_lds_dwordx4: lane i of a wave writes LDS bytes base + 16*i).
+// Each lane loads the 16-byte chunk that the swizzle places at its LDS slot.
+// Rows at or past n_rows read row n_rows - 1 (finite data that the caller
+// masks), so no load leaves the tensor. The caller waits (s_waitcnt) and
+// synchronises before reading the tile.
+template <int D, int ROWS, int NW>
+__device__ __forceinline__ void dma_tile(char* lds_tile, const bf16* g, int64_t rs, int row0, int n_rows,
+                                         int w, int lane) {
+  constexpr int BYTES = ROWS * D * 2;
+  constexpr int PER_WAVE = BYTES / (1024 * NW);
+  static_assert(BYTES % (1024 * NW) == 0, "tile must split into 1 KB pieces per wave");
+#pragma unroll
+  for (int n = 0; n < PER_WAVE; ++n) {
+    const int m = w * PER_WAVE + n;
+    const int byte = m * 1024 + 16 * lane;
+    const int r = byte / (2 * D);
+    const int slot = (byte % (2 * D)) >> 4;
+    const int cc = slot ^ tile_swz<D>(r);
+    const int row = min(row0 + r, n_rows - 1);
+    const bf16* src = g + (int64_t)row * rs + cc * 8;
+    __builtin_amdgcn_global_load_lds((const void FA2_GLOBAL*)src, (void FA2_LDS*)(lds_tile + m * 1024), 16, 0, 0);
+  }
+}
+
+// Wait for every outstanding memory operation of this wave (including direct
+// global->LDS loads), then synchronise the workgroup.
+__device__ __forceinline__ void wait_all_and_sync() {
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+}
+
+// Hides a value from the optimiser so that expressions built from it are
+// recomputed where they are used instead of being hoisted (and kept live)
+// across a loop.
+template <typename T>
+__device__ __forceinline__ void opaque(T& x) {
+  asm volatile("" : "+v"(x));
 }
 
 struct FwdParams {

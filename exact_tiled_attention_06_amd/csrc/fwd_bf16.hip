@@ -31,6 +31,8 @@
 //    bank conflicts.
 //  * Causal / windowed grids run the longest query blocks first; masks are
 //    evaluated only on tiles that cross a mask edge or the end of the sequence.
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -38,29 +40,17 @@ namespace fa2 {
 
 constexpr float kRescaleLog2 = 8.0f;
 
-// 16-byte chunk position of chunk `cc` of row `r` in an LDS tile.
-template <int D>
-__device__ __forceinline__ int k_swz(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
-template <int D>
-__device__ __forceinline__ int v_swz(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
-
-template <int D>
-__device__ __forceinline__ uint32_t k_off(int r, int cc) { return r * (D * 2) + ((cc ^ k_swz<D>(r)) << 4); }
-template <int D>
-__device__ __forceinline__ uint32_t v_off(int r, int cc) { return r * (D * 2) + ((cc ^ v_swz<D>(r)) << 4); }
-
 template <int D, int NW, int BC>
 struct FwdShape {
   static constexpr int NT = NW * 64;        // threads
   static constexpr int BR = NW * 32;        // query rows per workgroup
-  static constexpr int CPR = D / 8;         // 16-byte chunks per row
   static constexpr int TILE = BC * D * 2;   // bytes of one K (or V) tile
-  static constexpr int CPT = BC * CPR / NT; // chunks per thread per tile
   static constexpr int NSUB = BC / 32;      // 32-key subtiles per tile
   static constexpr int KS = D / 16;         // MFMA reduction steps over d
   static constexpr int MB = D / 32;         // 32-row blocks of O^T
-  static constexpr int LDS = 2 * 2 * TILE;  // two stages of K and V
-  static_assert((BC * CPR) % NT == 0, "tile must split evenly over threads");
+  static constexpr int STAGE = 2 * TILE;    // K and V of one tile
+  static constexpr int LDS = 2 * STAGE;     // two stages
+  static constexpr int ROWB = 2 * D;        // bytes per LDS row
 };
 
 template <int D, int NW, int BC, bool ALIBI>
@@ -76,6 +66,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdParams p) {
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
+  const int g = lane >> 4, j = lane & 15;
   const int64_t rs = (int64_t)p.H * D;  // elements between consecutive tokens
   const int64_t base = (int64_t)b * N * rs + (int64_t)h * D;
   const bf16* qg = (const bf16*)p.q + base;
@@ -94,15 +85,9 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdParams p) {
   bf16x8 qf[S::KS];
 #pragma unroll
   for (int ks = 0; ks < S::KS; ++ks) {
-    if (qi < N) {
-      qf[ks] = *reinterpret_cast<const bf16x8*>(qg + (int64_t)qi * rs + 16 * ks + 8 * hh);
-    } else {
-      qf[ks] = bf16x8{};
-    }
+    qf[ks] = qi < N ? *reinterpret_cast<const bf16x8*>(qg + (int64_t)qi * rs + 16 * ks + 8 * hh) : bf16x8{};
   }
-
-  float slope2 = 0.f;
-  if (ALIBI) slope2 = p.alibi[h] * kLog2e;
+  const float slope2 = ALIBI ? p.alibi[h] * kLog2e : 0.f;
 
   // Visible key range of the whole block.
   int kv_lo = 0, kv_hi = N;
@@ -110,44 +95,32 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdParams p) {
   if (p.wr >= 0) kv_hi = min(N, q_last + p.wr + 1);
   const int t_lo = kv_lo / BC, t_hi = (kv_hi + BC - 1) / BC;
 
+  // Per-lane LDS bases; every read below is base ^ (compile-time constant).
+  //  K (A operand of S^T): row kperm(l32) (+32*sub), chunk 2*ks + hh.
+  const int kr = kperm(l32);
+  uint32_t kbase = kr * S::ROWB + ((hh ^ tile_swz<D>(kr)) << 4);
+  //  V (transposed reads): rows 8*hh + j/4 (+4), columns 16*(g&1) + 4*(j&3) (+32*mb).
+  const int vr0 = 8 * hh + (j >> 2);
+  const int c0 = 2 * (g & 1) + ((j & 3) >> 1);
+  uint32_t vbase_lo = vr0 * S::ROWB + ((c0 ^ tile_swz<D>(vr0)) << 4) + (j & 1) * 8;
+  uint32_t vbase_hi = (vr0 + 4) * S::ROWB + ((c0 ^ tile_swz<D>(vr0 + 4)) << 4) + (j & 1) * 8;
+
   f32x16 o[S::MB];
 #pragma unroll
   for (int mb = 0; mb < S::MB; ++mb) o[mb] = f32x16{};
   float m2 = kNoMax;  // running max, log2 units
   float l = 0.f;      // running sum (this lane half's keys)
 
-  u32x4 kr[S::CPT], vr[S::CPT];
-  auto load_tile = [&](int t) {
-#pragma unroll
-    for (int i = 0; i < S::CPT; ++i) {
-      const int c = tid + i * S::NT;
-      const int r = c / S::CPR, cc = c % S::CPR;
-      const int key = t * BC + r;
-      if (key < N) {
-        kr[i] = *reinterpret_cast<const u32x4*>(kg + (int64_t)key * rs + cc * 8);
-        vr[i] = *reinterpret_cast<const u32x4*>(vg + (int64_t)key * rs + cc * 8);
-      } else {
-        kr[i] = u32x4{0, 0, 0, 0};
-        vr[i] = u32x4{0, 0, 0, 0};
-      }
-    }
-  };
-  auto store_tile = [&](int stage) {
-    char* kb = smem + stage * 2 * S::TILE;
-    char* vb = kb + S::TILE;
-#pragma unroll
-    for (int i = 0; i < S::CPT; ++i) {
-      const int c = tid + i * S::NT;
-      const int r = c / S::CPR, cc = c % S::CPR;
-      *reinterpret_cast<u32x4*>(kb + k_off<D>(r, cc)) = kr[i];
-      *reinterpret_cast<u32x4*>(vb + v_off<D>(r, cc)) = vr[i];
-    }
+  auto issue_tile = [&](int t, int stage) {
+    char* kb = smem + stage * S::STAGE;
+    dma_tile<D, BC, NW>(kb, kg, rs, t * BC, N, w, lane);
+    dma_tile<D, BC, NW>(kb + S::TILE, vg, rs, t * BC, N, w, lane);
   };
 
   // One tile of the online softmax for this wave.
   auto compute = [&](int stage, int j0, auto masked_tag) {
     constexpr bool MASKED = decltype(masked_tag)::value;
-    const char* kb = smem + stage * 2 * S::TILE;
+    const char* kb = smem + stage * S::STAGE;
     const char* vb = kb + S::TILE;
 
     // S^T = K Q^T for each 32-key subtile.
@@ -155,10 +128,9 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdParams p) {
 #pragma unroll
     for (int sub = 0; sub < S::NSUB; ++sub) {
       s[sub] = f32x16{};
-      const int krow = 32 * sub + kperm(l32);
 #pragma unroll
       for (int ks = 0; ks < S::KS; ++ks) {
-        const bf16x8 a = lds_read16(kb, k_off<D>(krow, 2 * ks + hh));
+        const bf16x8 a = lds_read16(kb, kbase ^ ((ks << 5) | (sub * 32 * S::ROWB)));
         s[sub] = mfma32(a, qf[ks], s[sub]);
       }
     }
@@ -195,7 +167,6 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdParams p) {
     }
 
     // P = exp2(y - m2), running sum, then O^T += V^T P^T.
-    const int g = lane >> 4, j = lane & 15;
 #pragma unroll
     for (int sub = 0; sub < S::NSUB; ++sub) {
 #pragma unroll
@@ -209,13 +180,11 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdParams p) {
         const bf16x8 pb = pack_bf16x8(s[sub][8 * kk + 0], s[sub][8 * kk + 1], s[sub][8 * kk + 2],
                                       s[sub][8 * kk + 3], s[sub][8 * kk + 4], s[sub][8 * kk + 5],
                                       s[sub][8 * kk + 6], s[sub][8 * kk + 7]);
-        const int vrow = 32 * sub + 16 * kk + 8 * hh + (j >> 2);
+        const uint32_t rowoff = (2 * sub + kk) * 16 * S::ROWB;
 #pragma unroll
         for (int mb = 0; mb < S::MB; ++mb) {
-          const int dcol = 32 * mb + 16 * (g & 1) + 4 * (j & 3);
-          const uint32_t in_chunk = (dcol & 7) * 2;
-          const bf16x4 lo = lds_read_tr(vb + v_off<D>(vrow, dcol >> 3) + in_chunk);
-          const bf16x4 hi = lds_read_tr(vb + v_off<D>(vrow + 4, dcol >> 3) + in_chunk);
+          const bf16x4 lo = lds_read_tr(vb + (vbase_lo ^ ((mb << 6) | rowoff)));
+          const bf16x4 hi = lds_read_tr(vb + (vbase_hi ^ ((mb << 6) | rowoff)));
           const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
           o[mb] = mfma32(a, pb, o[mb]);
         }
@@ -223,13 +192,14 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdParams p) {
     }
   };
 
-  load_tile(t_lo);
-  store_tile(0);
-  __syncthreads();
+  issue_tile(t_lo, 0);
+  wait_all_and_sync();
   for (int t = t_lo; t < t_hi; ++t) {
     const int stage = (t - t_lo) & 1;
-    const bool more = t + 1 < t_hi;
-    if (more) load_tile(t + 1);
+    if (t + 1 < t_hi) issue_tile(t + 1, stage ^ 1);
+    opaque(kbase);
+    opaque(vbase_lo);
+    opaque(vbase_hi);
     const int j0 = t * BC;
     const int j1 = j0 + BC - 1;
     const bool skip = !wave_live || (p.wr >= 0 && j0 > wq_last + p.wr) || (p.wl >= 0 && j1 < qw0 - p.wl);
@@ -241,8 +211,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdParams p) {
         compute(stage, j0, std::true_type{});
       }
     }
-    if (more) store_tile(stage ^ 1);
-    __syncthreads();
+    wait_all_and_sync();
   }
 
   if (!wave_live) return;

@@ -124,7 +124,7 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void bwd_main_kernel(BwdPara
   const int b = bh / p.H, h = bh % p.H;
   const int N = p.N;
   const int tid = threadIdx.x;
-  const int w = tid >> 6, lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
   const int g = lane >> 4, j = lane & 15;
   const int64_t rs = (int64_t)p.H * D;
   const int64_t base = (int64_t)b * N * rs + (int64_t)h * D;
@@ -181,12 +181,36 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void bwd_main_kernel(BwdPara
     dv[mb] = f32x16{};
   }
 
+  // Per-lane byte offsets of this lane's direct-load pieces of a Q/dO tile.
+  constexpr int PER_WAVE = S::QT_BYTES / (1024 * S::NW);
+  uint32_t dma_off[PER_WAVE];
+#pragma unroll
+  for (int n = 0; n < PER_WAVE; ++n) {
+    const int byte = (w * PER_WAVE + n) * 1024 + 16 * lane;
+    const int r = byte / ROWB;
+    const int cc = ((byte % ROWB) >> 4) ^ tile_swz<D>(r);
+    dma_off[n] = (uint32_t)(r * rs * 2 + cc * 16);
+  }
+
   // Q, dO (swizzled tiles) and LSE, D (raw floats) of query block `it` into a stage.
-  auto issue_q = [&](int it, int stage) {
-    char* st = stage_lds + stage * S::STAGE_BYTES;
+  auto issue_q = [&](int it, auto stage_c) {
+    constexpr int stg = decltype(stage_c)::value;
+    char* st = stage_lds + stg * S::STAGE_BYTES;
     const int i0 = it * S::BQ;
-    dma_tile<D, S::BQ, S::NW>(st, qg, rs, i0, N, w, lane);
-    dma_tile<D, S::BQ, S::NW>(st + S::QT_BYTES, dog, rs, i0, N, w, lane);
+    if (i0 + S::BQ <= N) {
+      const char* qgb = reinterpret_cast<const char*>(qg + (int64_t)i0 * rs);
+      const char* ogb = reinterpret_cast<const char*>(dog + (int64_t)i0 * rs);
+#pragma unroll
+      for (int n = 0; n < PER_WAVE; ++n) {
+        char* dst = st + (w * PER_WAVE + n) * 1024;
+        __builtin_amdgcn_global_load_lds((const void FA2_GLOBAL*)(qgb + dma_off[n]), (void FA2_LDS*)dst, 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void FA2_GLOBAL*)(ogb + dma_off[n]),
+                                         (void FA2_LDS*)(dst + S::QT_BYTES), 16, 0, 0);
+      }
+    } else {  // last, partial block: clamp rows to the sequence
+      dma_tile<D, S::BQ, S::NW>(st, qg, rs, i0, N, w, lane);
+      dma_tile<D, S::BQ, S::NW>(st + S::QT_BYTES, dog, rs, i0, N, w, lane);
+    }
     if (w == 0) {
       const int q = min(i0 + l32, N - 1);
       const float* src = hh ? del_g + q : lse_g + q;
@@ -194,85 +218,10 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void bwd_main_kernel(BwdPara
     }
   };
 
-  auto compute = [&](int stage, int i0, auto masked_tag) {
-    constexpr bool MASKED = decltype(masked_tag)::value;
-    const char* q_t = stage_lds + stage * S::STAGE_BYTES;
-    const char* do_t = q_t + S::QT_BYTES;
-    const float* lse_t = reinterpret_cast<const float*>(q_t + 2 * S::QT_BYTES);
-    const float* del_t = lse_t + S::BQ;
-
-    // S = Q K^T: rows are queries (A lane m reads row kperm(m)), columns are this wave's keys.
-    f32x16 s = f32x16{};
-#pragma unroll
-    for (int ks = 0; ks < S::KS; ++ks) {
-      const bf16x8 a = lds_read16(q_t, qa_base ^ (ks << 5));
-      const bf16x8 bk = lds_read16(k_lds, kb_base ^ (ks << 5));
-      s = mfma32(a, bk, s);
-    }
-    // P = exp2(S*scale*log2e + bias - LSE*log2e), zero where masked.
-    float pr[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int qr = key_of_reg(r, hh);  // query row within the block held by register r
-      const int q = i0 + qr;
-      float y = s[r] * p.scale_log2;
-      if (ALIBI) y = fmaf(-slope2, fabsf((float)(q - kj)), y);
-      float pv = fast_exp2(fmaf(lse_t[qr], -kLog2e, y));
-      if (MASKED) {
-        const bool vis = q < N && kj < N && (p.wr < 0 || kj <= q + p.wr) && (p.wl < 0 || kj >= q - p.wl);
-        pv = vis ? pv : 0.f;
-      }
-      pr[r] = pv;
-    }
-    // dP = dO V^T, then dS = P * (dP - D).
-    f32x16 dp = f32x16{};
-#pragma unroll
-    for (int ks = 0; ks < S::KS; ++ks) {
-      const bf16x8 ao = lds_read16(do_t, qa_base ^ (ks << 5));
-      dp = mfma32(ao, vf[ks], dp);
-    }
-    bf16x8 pb[2], dsb[2];
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      float d8[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int r = 8 * kk + e;
-        d8[e] = pr[r] * (dp[r] - del_t[key_of_reg(r, hh)]);
-      }
-      pb[kk] = pack_bf16x8(pr[8 * kk], pr[8 * kk + 1], pr[8 * kk + 2], pr[8 * kk + 3], pr[8 * kk + 4],
-                           pr[8 * kk + 5], pr[8 * kk + 6], pr[8 * kk + 7]);
-      dsb[kk] = pack_bf16x8(d8[0], d8[1], d8[2], d8[3], d8[4], d8[5], d8[6], d8[7]);
-    }
-    if (!DET) {
-      const int row = 32 * w + l32;  // key row of dS^T; chunk c holds queries 8c .. 8c+7
-      *reinterpret_cast<bf16x8*>(ds_lds + ds_off(row, hh)) = dsb[0];
-      *reinterpret_cast<bf16x8*>(ds_lds + ds_off(row, 2 + hh)) = dsb[1];
-    }
-    // dV^T += dO^T P and dK^T += Q^T dS (A operands read transposed from LDS).
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-#pragma unroll
-      for (int mb = 0; mb < S::MB; ++mb) {
-        const uint32_t x = (mb << 6) | (kk * 16 * ROWB);
-        const bf16x4 o_lo = lds_read_tr(do_t + (tr_lo ^ x));
-        const bf16x4 o_hi = lds_read_tr(do_t + (tr_hi ^ x));
-        const bf16x8 ao = {o_lo[0], o_lo[1], o_lo[2], o_lo[3], o_hi[0], o_hi[1], o_hi[2], o_hi[3]};
-        dv[mb] = mfma32(ao, pb[kk], dv[mb]);
-        const bf16x4 q_lo = lds_read_tr(q_t + (tr_lo ^ x));
-        const bf16x4 q_hi = lds_read_tr(q_t + (tr_hi ^ x));
-        const bf16x8 aq = {q_lo[0], q_lo[1], q_lo[2], q_lo[3], q_hi[0], q_hi[1], q_hi[2], q_hi[3]};
-        dk[mb] = mfma32(aq, dsb[kk], dk[mb]);
-      }
-    }
-  };
-
-  issue_q(it_lo, 0);
-  wait_all_and_sync();
-  for (int it = it_lo; it < it_hi; ++it) {
-    const int stage = (it - it_lo) & 1;
-    const bool more = it + 1 < it_hi;
-    if (more) issue_q(it + 1, stage ^ 1);
+  // One 32-query block; the stage is a compile-time constant.
+  auto body = [&](int it, auto stage_c) {
+    constexpr int stg = decltype(stage_c)::value;
+    if (it + 1 < it_hi) issue_q(it + 1, std::integral_constant<int, stg ^ 1>{});
     opaque(qa_base);
     opaque(kb_base);
     opaque(tr_lo);
@@ -281,12 +230,85 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void bwd_main_kernel(BwdPara
     const int i1 = i0 + S::BQ - 1;
     const bool skip = kw0 >= N || (p.wr >= 0 && i1 + p.wr < kw0) || (p.wl >= 0 && i0 - p.wl > kw0 + 31);
     if (!skip) {
+      const char* q_t = stage_lds + stg * S::STAGE_BYTES;
+      const char* do_t = q_t + S::QT_BYTES;
+      const float* lse_t = reinterpret_cast<const float*>(q_t + 2 * S::QT_BYTES);
+      const float* del_t = lse_t + S::BQ;
+
+      uint32_t qx[S::KS];
+#pragma unroll
+      for (int ks = 0; ks < S::KS; ++ks) qx[ks] = qa_base ^ (ks << 5);
+      // S = Q K^T: rows are queries (A lane m reads row kperm(m)), columns are this wave's keys.
+      f32x16 s = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < S::KS; ++ks) {
+        const bf16x8 a = lds_read16(q_t, qx[ks]);
+        const bf16x8 bk = lds_read16(k_lds, kb_base ^ (ks << 5));
+        s = mfma32(a, bk, s);
+      }
+      // P = exp2(S*scale*log2e + bias - LSE*log2e).
+      float pr[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int qr = key_of_reg(r, hh);  // query row within the block held by register r
+        float y = s[r] * p.scale_log2;
+        if (ALIBI) y = fmaf(-slope2, fabsf((float)(i0 + qr - kj)), y);
+        pr[r] = fast_exp2(fmaf(lse_t[qr], -kLog2e, y));
+      }
       const bool full = i1 < N && kw0 + 31 < N && (p.wr < 0 || i0 + p.wr >= kw0 + 31) &&
                         (p.wl < 0 || i1 - p.wl <= kw0);
-      if (full) {
-        compute(stage, i0, std::false_type{});
-      } else {
-        compute(stage, i0, std::true_type{});
+      if (!full) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int q = i0 + key_of_reg(r, hh);
+          const bool vis = q < N && kj < N && (p.wr < 0 || kj <= q + p.wr) && (p.wl < 0 || kj >= q - p.wl);
+          pr[r] = vis ? pr[r] : 0.f;
+        }
+      }
+      // dP = dO V^T, then dS = P * (dP - D).
+      f32x16 dp = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < S::KS; ++ks) {
+        const bf16x8 ao = lds_read16(do_t, qx[ks]);
+        dp = mfma32(ao, vf[ks], dp);
+      }
+      bf16x8 pb[2], dsb[2];
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        float d8[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int r = 8 * kk + e;
+          d8[e] = pr[r] * (dp[r] - del_t[key_of_reg(r, hh)]);
+        }
+        pb[kk] = pack_bf16x8(pr[8 * kk], pr[8 * kk + 1], pr[8 * kk + 2], pr[8 * kk + 3], pr[8 * kk + 4],
+                             pr[8 * kk + 5], pr[8 * kk + 6], pr[8 * kk + 7]);
+        dsb[kk] = pack_bf16x8(d8[0], d8[1], d8[2], d8[3], d8[4], d8[5], d8[6], d8[7]);
+      }
+      if (!DET) {
+        const int row = 32 * w + l32;  // key row of dS^T; chunk c holds queries 8c .. 8c+7
+        *reinterpret_cast<bf16x8*>(ds_lds + ds_off(row, hh)) = dsb[0];
+        *reinterpret_cast<bf16x8*>(ds_lds + ds_off(row, 2 + hh)) = dsb[1];
+      }
+      // dV^T += dO^T P and dK^T += Q^T dS (A operands read transposed from LDS).
+      uint32_t tx_lo[S::MB], tx_hi[S::MB];
+#pragma unroll
+      for (int mb = 0; mb < S::MB; ++mb) {
+        tx_lo[mb] = tr_lo ^ (mb << 6);
+        tx_hi[mb] = tr_hi ^ (mb << 6);
+      }
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+        for (int mb = 0; mb < S::MB; ++mb) {
+          const int ro = kk * 16 * ROWB;
+          const bf16x4 o_lo = lds_read_tr(do_t + ro + tx_lo[mb]);
+          const bf16x4 o_hi = lds_read_tr(do_t + ro + tx_hi[mb]);
+          dv[mb] = mfma32(__builtin_shufflevector(o_lo, o_hi, 0, 1, 2, 3, 4, 5, 6, 7), pb[kk], dv[mb]);
+          const bf16x4 q_lo = lds_read_tr(q_t + ro + tx_lo[mb]);
+          const bf16x4 q_hi = lds_read_tr(q_t + ro + tx_hi[mb]);
+          dk[mb] = mfma32(__builtin_shufflevector(q_lo, q_hi, 0, 1, 2, 3, 4, 5, 6, 7), dsb[kk], dk[mb]);
+        }
       }
     } else if (!DET) {
       const int row = 32 * w + l32;
@@ -307,9 +329,8 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void bwd_main_kernel(BwdPara
         const bf16x4 a_hi = lds_read_tr(ds_lds + ds_hi + kk * 16 * 64);
         const bf16x4 b_lo = lds_read_tr(k_lds + kt_lo + kk * 16 * ROWB);
         const bf16x4 b_hi = lds_read_tr(k_lds + kt_hi + kk * 16 * ROWB);
-        const bf16x8 a = {a_lo[0], a_lo[1], a_lo[2], a_lo[3], a_hi[0], a_hi[1], a_hi[2], a_hi[3]};
-        const bf16x8 bb = {b_lo[0], b_lo[1], b_lo[2], b_lo[3], b_hi[0], b_hi[1], b_hi[2], b_hi[3]};
-        dqa = mfma32(a, bb, dqa);
+        dqa = mfma32(__builtin_shufflevector(a_lo, a_hi, 0, 1, 2, 3, 4, 5, 6, 7),
+                     __builtin_shufflevector(b_lo, b_hi, 0, 1, 2, 3, 4, 5, 6, 7), dqa);
       }
       float* dq_row = p.dq_acc + ((int64_t)bh * N + i0) * D + 32 * mbq + l32;
 #pragma unroll
@@ -319,6 +340,13 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void bwd_main_kernel(BwdPara
       }
     }
     wait_all_and_sync();
+  };
+
+  issue_q(it_lo, std::integral_constant<int, 0>{});
+  wait_all_and_sync();
+  for (int it = it_lo; it < it_hi; it += 2) {
+    body(it, std::integral_constant<int, 0>{});
+    if (it + 1 < it_hi) body(it + 1, std::integral_constant<int, 1>{});
   }
 
   // dK = scale * dK^T, dV = dV^T, stored as bf16: lane holds key kj, d = 32*mb + 8*a + 4*hh + (0..3).
@@ -359,7 +387,7 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void bwd_dq_det_kernel(BwdPa
   const int b = bh / p.H, h = bh % p.H;
   const int N = p.N;
   const int tid = threadIdx.x;
-  const int w = tid >> 6, lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
   const int g = lane >> 4, j = lane & 15;
   const int64_t rs = (int64_t)p.H * D;
   const int64_t base = (int64_t)b * N * rs + (int64_t)h * D;
@@ -465,7 +493,7 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void bwd_dq_det_kernel(BwdPa
         const int col = 32 * mb + 16 * (g & 1) + 4 * (j & 3);
         const bf16x4 lo = lds_read_tr(kb + tile_off_tr<D>(row, col));
         const bf16x4 hi = lds_read_tr(kb + tile_off_tr<D>(row + 4, col));
-        const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         acc[mb] = mfma32(a, dsb, acc[mb]);
       }
     }

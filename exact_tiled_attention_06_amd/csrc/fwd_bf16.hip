@@ -56,6 +56,7 @@ struct FwdShape {
 template <int D, int NW, int BC, bool ALIBI>
 __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdParams p) {
   using S = FwdShape<D, NW, BC>;
+  constexpr int PER_WAVE = S::TILE / (1024 * NW);  // 1 KB direct-load pieces per wave per tensor
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
   const int bh_count = p.B * p.H;
@@ -65,7 +66,8 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdParams p) {
   const int N = p.N;
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6, lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
+  const int lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
   const int g = lane >> 4, j = lane & 15;
   const int64_t rs = (int64_t)p.H * D;  // elements between consecutive tokens
   const int64_t base = (int64_t)b * N * rs + (int64_t)h * D;
@@ -95,11 +97,21 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdParams p) {
   if (p.wr >= 0) kv_hi = min(N, q_last + p.wr + 1);
   const int t_lo = kv_lo / BC, t_hi = (kv_hi + BC - 1) / BC;
 
-  // Per-lane LDS bases; every read below is base ^ (compile-time constant).
+  // Per-lane byte offsets of this lane's direct-load pieces, relative to a tile's first row.
+  uint32_t dma_off[PER_WAVE];
+#pragma unroll
+  for (int n = 0; n < PER_WAVE; ++n) {
+    const int byte = (w * PER_WAVE + n) * 1024 + 16 * lane;
+    const int r = byte / S::ROWB;
+    const int cc = ((byte % S::ROWB) >> 4) ^ tile_swz<D>(r);
+    dma_off[n] = (uint32_t)(r * rs * 2 + cc * 16);
+  }
+
+  // Per-lane LDS bases; every read below is (base ^ small constant) + immediate.
   //  K (A operand of S^T): row kperm(l32) (+32*sub), chunk 2*ks + hh.
   const int kr = kperm(l32);
   uint32_t kbase = kr * S::ROWB + ((hh ^ tile_swz<D>(kr)) << 4);
-  //  V (transposed reads): rows 8*hh + j/4 (+4), columns 16*(g&1) + 4*(j&3) (+32*mb).
+  //  V (transposed reads): rows 8*hh + j/4 (+4) (+16*(2*sub + kk)), columns 16*(g&1) + 4*(j&3) (+32*mb).
   const int vr0 = 8 * hh + (j >> 2);
   const int c0 = 2 * (g & 1) + ((j & 3) >> 1);
   uint32_t vbase_lo = vr0 * S::ROWB + ((c0 ^ tile_swz<D>(vr0)) << 4) + (j & 1) * 8;
@@ -108,95 +120,33 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdParams p) {
   f32x16 o[S::MB];
 #pragma unroll
   for (int mb = 0; mb < S::MB; ++mb) o[mb] = f32x16{};
-  float m2 = kNoMax;  // running max, log2 units
-  float l = 0.f;      // running sum (this lane half's keys)
+  float m2 = kNoMax;                   // running max, log2 units
+  float lsum[4] = {0.f, 0.f, 0.f, 0.f};  // running sum (this lane half's keys), 4 partial sums
 
-  auto issue_tile = [&](int t, int stage) {
-    char* kb = smem + stage * S::STAGE;
-    dma_tile<D, BC, NW>(kb, kg, rs, t * BC, N, w, lane);
-    dma_tile<D, BC, NW>(kb + S::TILE, vg, rs, t * BC, N, w, lane);
-  };
-
-  // One tile of the online softmax for this wave.
-  auto compute = [&](int stage, int j0, auto masked_tag) {
-    constexpr bool MASKED = decltype(masked_tag)::value;
-    const char* kb = smem + stage * S::STAGE;
-    const char* vb = kb + S::TILE;
-
-    // S^T = K Q^T for each 32-key subtile.
-    f32x16 s[S::NSUB];
+  auto issue = [&](int t, auto stage_c) {
+    constexpr int st = decltype(stage_c)::value;
+    char* kl = smem + st * S::STAGE;
+    const int row0 = t * BC;
+    if (row0 + BC <= N) {
+      const char* kgb = reinterpret_cast<const char*>(kg + (int64_t)row0 * rs);
+      const char* vgb = reinterpret_cast<const char*>(vg + (int64_t)row0 * rs);
 #pragma unroll
-    for (int sub = 0; sub < S::NSUB; ++sub) {
-      s[sub] = f32x16{};
-#pragma unroll
-      for (int ks = 0; ks < S::KS; ++ks) {
-        const bf16x8 a = lds_read16(kb, kbase ^ ((ks << 5) | (sub * 32 * S::ROWB)));
-        s[sub] = mfma32(a, qf[ks], s[sub]);
+      for (int n = 0; n < PER_WAVE; ++n) {
+        char* dst = kl + (w * PER_WAVE + n) * 1024;
+        __builtin_amdgcn_global_load_lds((const void FA2_GLOBAL*)(kgb + dma_off[n]), (void FA2_LDS*)dst, 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void FA2_GLOBAL*)(vgb + dma_off[n]), (void FA2_LDS*)(dst + S::TILE),
+                                         16, 0, 0);
       }
-    }
-
-    // Mask, bias, row max.
-    float mx = -INFINITY;
-#pragma unroll
-    for (int sub = 0; sub < S::NSUB; ++sub) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float x = s[sub][r];
-        const int key = j0 + 32 * sub + key_of_reg(r, hh);
-        if (ALIBI) x = fmaf(x, p.scale_log2, -slope2 * fabsf((float)(qi - key)));
-        if (MASKED) {
-          const bool vis = key < N && (p.wr < 0 || key <= qi + p.wr) && (p.wl < 0 || key >= qi - p.wl);
-          x = vis ? x : -INFINITY;
-        }
-        s[sub][r] = x;
-        mx = fmaxf(mx, x);
-      }
-    }
-    if (!ALIBI) mx *= p.scale_log2;
-    mx = max_with_other_half(mx);
-
-    const float cand = fmaxf(m2, mx);
-    if (wave_any(cand - m2 > kRescaleLog2)) {
-      const float alpha = fast_exp2(m2 - cand);
-      m2 = cand;
-      l *= alpha;
-#pragma unroll
-      for (int mb = 0; mb < S::MB; ++mb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[mb][r] *= alpha;
-    }
-
-    // P = exp2(y - m2), running sum, then O^T += V^T P^T.
-#pragma unroll
-    for (int sub = 0; sub < S::NSUB; ++sub) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float pv = ALIBI ? fast_exp2(s[sub][r] - m2) : fast_exp2(fmaf(s[sub][r], p.scale_log2, -m2));
-        s[sub][r] = pv;
-        l += pv;
-      }
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const bf16x8 pb = pack_bf16x8(s[sub][8 * kk + 0], s[sub][8 * kk + 1], s[sub][8 * kk + 2],
-                                      s[sub][8 * kk + 3], s[sub][8 * kk + 4], s[sub][8 * kk + 5],
-                                      s[sub][8 * kk + 6], s[sub][8 * kk + 7]);
-        const uint32_t rowoff = (2 * sub + kk) * 16 * S::ROWB;
-#pragma unroll
-        for (int mb = 0; mb < S::MB; ++mb) {
-          const bf16x4 lo = lds_read_tr(vb + (vbase_lo ^ ((mb << 6) | rowoff)));
-          const bf16x4 hi = lds_read_tr(vb + (vbase_hi ^ ((mb << 6) | rowoff)));
-          const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          o[mb] = mfma32(a, pb, o[mb]);
-        }
-      }
+    } else {  // last, partial tile: clamp rows to the sequence
+      dma_tile<D, BC, NW>(kl, kg, rs, row0, N, w, lane);
+      dma_tile<D, BC, NW>(kl + S::TILE, vg, rs, row0, N, w, lane);
     }
   };
 
-  issue_tile(t_lo, 0);
-  wait_all_and_sync();
-  for (int t = t_lo; t < t_hi; ++t) {
-    const int stage = (t - t_lo) & 1;
-    if (t + 1 < t_hi) issue_tile(t + 1, stage ^ 1);
+  // One tile of the online softmax for this wave; the stage is a compile-time constant.
+  auto body = [&](int t, auto stage_c) {
+    constexpr int st = decltype(stage_c)::value;
+    if (t + 1 < t_hi) issue(t + 1, std::integral_constant<int, st ^ 1>{});
     opaque(kbase);
     opaque(vbase_lo);
     opaque(vbase_hi);
@@ -204,18 +154,107 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdParams p) {
     const int j1 = j0 + BC - 1;
     const bool skip = !wave_live || (p.wr >= 0 && j0 > wq_last + p.wr) || (p.wl >= 0 && j1 < qw0 - p.wl);
     if (!skip) {
+      const char* kb = smem + st * S::STAGE;
+      const char* vb = kb + S::TILE;
+
+      // S^T = K Q^T for each 32-key subtile.
+      f32x16 s[S::NSUB];
+#pragma unroll
+      for (int sub = 0; sub < S::NSUB; ++sub) s[sub] = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < S::KS; ++ks) {
+        const uint32_t ka = kbase ^ (ks << 5);
+#pragma unroll
+        for (int sub = 0; sub < S::NSUB; ++sub) {
+          const bf16x8 a = lds_read16(kb + sub * 32 * S::ROWB, ka);
+          s[sub] = mfma32(a, qf[ks], s[sub]);
+        }
+      }
+
+      // Bias (ALiBi, in log2 units) and masks; masks only on tiles crossing an edge.
+      if (ALIBI) {
+#pragma unroll
+        for (int sub = 0; sub < S::NSUB; ++sub)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = j0 + 32 * sub + key_of_reg(r, hh);
+            s[sub][r] = fmaf(s[sub][r], p.scale_log2, -slope2 * fabsf((float)(qi - key)));
+          }
+      }
       const bool full = j1 < N && (p.wr < 0 || j1 <= qw0 + p.wr) && (p.wl < 0 || j0 >= wq_last - p.wl);
-      if (full) {
-        compute(stage, j0, std::false_type{});
-      } else {
-        compute(stage, j0, std::true_type{});
+      if (!full) {
+#pragma unroll
+        for (int sub = 0; sub < S::NSUB; ++sub)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = j0 + 32 * sub + key_of_reg(r, hh);
+            const bool vis = key < N && (p.wr < 0 || key <= qi + p.wr) && (p.wl < 0 || key >= qi - p.wl);
+            s[sub][r] = vis ? s[sub][r] : -INFINITY;
+          }
+      }
+
+      // Row max; rescale the output only when some row's max grew past the threshold.
+      float mx = -INFINITY;
+#pragma unroll
+      for (int sub = 0; sub < S::NSUB; ++sub)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[sub][r]);
+      if (!ALIBI) mx *= p.scale_log2;
+      mx = max_with_other_half(mx);
+      const float cand = fmaxf(m2, mx);
+      if (wave_any(cand - m2 > kRescaleLog2)) {
+        const float alpha = fast_exp2(m2 - cand);
+        m2 = cand;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) lsum[i] *= alpha;
+#pragma unroll
+        for (int mb = 0; mb < S::MB; ++mb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[mb][r] *= alpha;
+      }
+
+      // P = exp2(y - m2); running sum in four independent partial sums; O^T += V^T P^T.
+      uint32_t vx_lo[S::MB], vx_hi[S::MB];
+#pragma unroll
+      for (int mb = 0; mb < S::MB; ++mb) {
+        vx_lo[mb] = vbase_lo ^ (mb << 6);
+        vx_hi[mb] = vbase_hi ^ (mb << 6);
+      }
+#pragma unroll
+      for (int sub = 0; sub < S::NSUB; ++sub) {
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          float pv[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float x = s[sub][8 * kk + e];
+            pv[e] = ALIBI ? fast_exp2(x - m2) : fast_exp2(fmaf(x, p.scale_log2, -m2));
+          }
+          const bf16x8 pb = pack_bf16x8(pv[0], pv[1], pv[2], pv[3], pv[4], pv[5], pv[6], pv[7]);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) lsum[e & 3] += pv[e];
+          const int rowoff = (2 * sub + kk) * 16 * S::ROWB;
+#pragma unroll
+          for (int mb = 0; mb < S::MB; ++mb) {
+            const bf16x4 lo = lds_read_tr(vb + rowoff + vx_lo[mb]);
+            const bf16x4 hi = lds_read_tr(vb + rowoff + vx_hi[mb]);
+            o[mb] = mfma32(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), pb, o[mb]);
+          }
+        }
       }
     }
     wait_all_and_sync();
+  };
+
+  issue(t_lo, std::integral_constant<int, 0>{});
+  wait_all_and_sync();
+  for (int t = t_lo; t < t_hi; t += 2) {
+    body(t, std::integral_constant<int, 0>{});
+    if (t + 1 < t_hi) body(t + 1, std::integral_constant<int, 1>{});
   }
 
   if (!wave_live) return;
-  const float lt = sum_with_other_half(l);
+  const float lt = sum_with_other_half((lsum[0] + lsum[1]) + (lsum[2] + lsum[3]));
   const float inv = lt > 0.f ? 1.0f / lt : 0.f;
   if (qi < N) {
     bf16* orow = og + (int64_t)qi * rs;

@@ -71,6 +71,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--deterministic", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB (3 launches), used to "
+                         "calibrate the FETCH_SIZE / WRITE_SIZE counters against a known byte count")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported (the path shards by "
@@ -78,6 +81,16 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.copy_probe:
+        n = args.copy_probe << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": n, "launches": 3}), flush=True)
+        return
 
     import exact_tiled_attention_06_amd as fa2
     import workloads

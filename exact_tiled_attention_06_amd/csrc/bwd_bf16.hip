@@ -33,6 +33,11 @@
 
 namespace fa2 {
 
+#ifndef FA2_HEAD_GROUP
+#define FA2_HEAD_GROUP 4
+#endif
+constexpr int kHeadGroup = FA2_HEAD_GROUP;  // heads walked together per XCD
+
 template <int D>
 struct BwdShape {
   static constexpr int NW = 4;
@@ -110,7 +115,7 @@ __global__ __launch_bounds__(256) void bwd_dq_convert_kernel(BwdParams p) {
 
 // ---------------------------------------------------------------- pass 2
 template <int D, bool ALIBI, bool DET>
-__global__ __launch_bounds__(256, D == 128 ? 1 : 2) void bwd_main_kernel(BwdParams p) {
+__global__ __launch_bounds__(256, (D == 128 && !DET) ? 1 : 2) void bwd_main_kernel(BwdParams p) {
   using S = BwdShape<D>;
   constexpr int ROWB = 2 * D;
   extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -118,9 +123,8 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void bwd_main_kernel(BwdPara
   char* stage_lds = smem + S::K_BYTES;
   char* ds_lds = stage_lds + 2 * S::STAGE_BYTES;
 
-  const int bh_count = p.B * p.H;
-  const int kb = (int)(blockIdx.x / bh_count);  // low key blocks see the most queries: first
-  const int bh = (int)(blockIdx.x % bh_count);
+  int bh, kb;
+  grid_map<kHeadGroup>((int)blockIdx.x, (p.N + S::BK - 1) / S::BK, p.B * p.H, false, bh, kb);  // early keys first
   const int b = bh / p.H, h = bh % p.H;
   const int N = p.N;
   const int tid = threadIdx.x;
@@ -371,23 +375,28 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void bwd_main_kernel(BwdPara
 }
 
 // ---------------------------------------------------------------- deterministic dQ
+// One workgroup per (batch, head, 128-query block); every wave owns 32 query
+// rows and sweeps the visible 32-key tiles like the forward: S^T = K Q^T and
+// dP^T = V dO^T put one query per lane (column), so LSE and D are per-lane
+// scalars, and dS^T feeds dQ^T += K^T dS^T as the B operand straight from
+// registers (K^T read transposed from the K tile).
 template <int D, bool ALIBI>
-__global__ __launch_bounds__(256, D == 128 ? 1 : 2) void bwd_dq_det_kernel(BwdParams p) {
-  constexpr int NW = 4, NT = 256, BR = NW * 32, BC = 32;
-  constexpr int CPR = D / 8, KS = D / 16, MB = D / 32;
+__global__ __launch_bounds__(256, 2) void bwd_dq_det_kernel(BwdParams p) {
+  constexpr int NW = 4, BR = NW * 32, BC = 32;
+  constexpr int KS = D / 16, MB = D / 32;
+  constexpr int ROWB = 2 * D;
   constexpr int TILE = BC * D * 2;
-  constexpr int CPT = BC * CPR / NT;
-  static_assert(BC * CPR % NT == 0, "even split");
+  constexpr int STAGE = 2 * TILE;
+  constexpr int PER_WAVE = TILE / (1024 * NW);
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
-  const int bh_count = p.B * p.H;
-  const int n_qblocks = (p.N + BR - 1) / BR;
-  const int qb = n_qblocks - 1 - (int)(blockIdx.x / bh_count);
-  const int bh = (int)(blockIdx.x % bh_count);
+  int bh, qb;
+  grid_map<kHeadGroup>((int)blockIdx.x, (p.N + BR - 1) / BR, p.B * p.H, true, bh, qb);
   const int b = bh / p.H, h = bh % p.H;
   const int N = p.N;
   const int tid = threadIdx.x;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
   const int g = lane >> 4, j = lane & 15;
   const int64_t rs = (int64_t)p.H * D;
   const int64_t base = (int64_t)b * N * rs + (int64_t)h * D;
@@ -406,13 +415,8 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void bwd_dq_det_kernel(BwdPa
   bf16x8 qf[KS], of[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
-    if (qi < N) {
-      qf[ks] = *reinterpret_cast<const bf16x8*>(qg + (int64_t)qi * rs + 16 * ks + 8 * hh);
-      of[ks] = *reinterpret_cast<const bf16x8*>(dog + (int64_t)qi * rs + 16 * ks + 8 * hh);
-    } else {
-      qf[ks] = bf16x8{};
-      of[ks] = bf16x8{};
-    }
+    qf[ks] = qi < N ? *reinterpret_cast<const bf16x8*>(qg + (int64_t)qi * rs + 16 * ks + 8 * hh) : bf16x8{};
+    of[ks] = qi < N ? *reinterpret_cast<const bf16x8*>(dog + (int64_t)qi * rs + 16 * ks + 8 * hh) : bf16x8{};
   }
   const float lse2 = qi < N ? p.lse[(int64_t)bh * N + qi] * kLog2e : INFINITY;
   const float delta = qi < N ? p.delta[(int64_t)bh * N + qi] : 0.f;
@@ -423,102 +427,111 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void bwd_dq_det_kernel(BwdPa
   if (p.wr >= 0) kv_hi = min(N, q_last + p.wr + 1);
   const int t_lo = kv_lo / BC, t_hi = (kv_hi + BC - 1) / BC;
 
+  uint32_t dma_off[PER_WAVE];
+#pragma unroll
+  for (int n = 0; n < PER_WAVE; ++n) {
+    const int byte = (w * PER_WAVE + n) * 1024 + 16 * lane;
+    const int r = byte / ROWB;
+    const int cc = ((byte % ROWB) >> 4) ^ tile_swz<D>(r);
+    dma_off[n] = (uint32_t)(r * rs * 2 + cc * 16);
+  }
+  const int kr = kperm(l32);
+  uint32_t abase = kr * ROWB + ((hh ^ tile_swz<D>(kr)) << 4);  // K, V rows (A operands)
+  const int tr0 = 8 * hh + (j >> 2);
+  const int c0 = 2 * (g & 1) + ((j & 3) >> 1);
+  uint32_t tr_lo = tr0 * ROWB + ((c0 ^ tile_swz<D>(tr0)) << 4) + (j & 1) * 8;
+  uint32_t tr_hi = (tr0 + 4) * ROWB + ((c0 ^ tile_swz<D>(tr0 + 4)) << 4) + (j & 1) * 8;
+
   f32x16 acc[MB];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) acc[mb] = f32x16{};
 
-  u32x4 kr[CPT], vr[CPT];
-  auto load_tile = [&](int t) {
+  auto issue = [&](int t, auto stage_c) {
+    constexpr int st = decltype(stage_c)::value;
+    char* kl = smem + st * STAGE;
+    const int row0 = t * BC;
+    if (row0 + BC <= N) {
+      const char* kgb = reinterpret_cast<const char*>(kg + (int64_t)row0 * rs);
+      const char* vgb = reinterpret_cast<const char*>(vg + (int64_t)row0 * rs);
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int c = tid + i * NT;
-      const int r = c / CPR, cc = c % CPR;
-      const int key = t * BC + r;
-      if (key < N) {
-        kr[i] = *reinterpret_cast<const u32x4*>(kg + (int64_t)key * rs + cc * 8);
-        vr[i] = *reinterpret_cast<const u32x4*>(vg + (int64_t)key * rs + cc * 8);
-      } else {
-        kr[i] = u32x4{0, 0, 0, 0};
-        vr[i] = u32x4{0, 0, 0, 0};
+      for (int n = 0; n < PER_WAVE; ++n) {
+        char* dst = kl + (w * PER_WAVE + n) * 1024;
+        __builtin_amdgcn_global_load_lds((const void FA2_GLOBAL*)(kgb + dma_off[n]), (void FA2_LDS*)dst, 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void FA2_GLOBAL*)(vgb + dma_off[n]), (void FA2_LDS*)(dst + TILE), 16,
+                                         0, 0);
       }
-    }
-  };
-  auto store_tile = [&](int stage) {
-    char* kb = smem + stage * 2 * TILE;
-    char* vb = kb + TILE;
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int c = tid + i * NT;
-      const int r = c / CPR, cc = c % CPR;
-      *reinterpret_cast<u32x4*>(kb + tile_off<D>(r, cc)) = kr[i];
-      *reinterpret_cast<u32x4*>(vb + tile_off<D>(r, cc)) = vr[i];
+    } else {
+      dma_tile<D, BC, NW>(kl, kg, rs, row0, N, w, lane);
+      dma_tile<D, BC, NW>(kl + TILE, vg, rs, row0, N, w, lane);
     }
   };
 
-  auto compute = [&](int stage, int j0, auto masked_tag) {
-    constexpr bool MASKED = decltype(masked_tag)::value;
-    const char* kb = smem + stage * 2 * TILE;
-    const char* vb = kb + TILE;
-    // S^T = K Q^T and dP^T = V dO^T: rows are keys (A lane m reads row kperm(m)), columns queries.
-    f32x16 s = f32x16{}, dp = f32x16{};
-    const int arow = kperm(l32);
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const bf16x8 ak = lds_read16(kb, tile_off<D>(arow, 2 * ks + hh));
-      s = mfma32(ak, qf[ks], s);
-      const bf16x8 av = lds_read16(vb, tile_off<D>(arow, 2 * ks + hh));
-      dp = mfma32(av, of[ks], dp);
-    }
-    float dsr[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int key = j0 + key_of_reg(r, hh);
-      float y = s[r] * p.scale_log2;
-      if (ALIBI) y = fmaf(-slope2, fabsf((float)(qi - key)), y);
-      float pv = fast_exp2(y - lse2);
-      if (MASKED) {
-        const bool vis = key < N && qi < N && (p.wr < 0 || key <= qi + p.wr) && (p.wl < 0 || key >= qi - p.wl);
-        pv = vis ? pv : 0.f;
-      }
-      dsr[r] = pv * (dp[r] - delta);
-    }
-    // dQ^T += K^T dS^T: A = K^T read transposed from the K tile, B = dS^T from registers.
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const bf16x8 dsb = pack_bf16x8(dsr[8 * kk], dsr[8 * kk + 1], dsr[8 * kk + 2], dsr[8 * kk + 3],
-                                     dsr[8 * kk + 4], dsr[8 * kk + 5], dsr[8 * kk + 6], dsr[8 * kk + 7]);
-      const int row = 16 * kk + 8 * hh + (j >> 2);
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        const int col = 32 * mb + 16 * (g & 1) + 4 * (j & 3);
-        const bf16x4 lo = lds_read_tr(kb + tile_off_tr<D>(row, col));
-        const bf16x4 hi = lds_read_tr(kb + tile_off_tr<D>(row + 4, col));
-        const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        acc[mb] = mfma32(a, dsb, acc[mb]);
-      }
-    }
-  };
-
-  load_tile(t_lo);
-  store_tile(0);
-  __syncthreads();
-  for (int t = t_lo; t < t_hi; ++t) {
-    const int stage = (t - t_lo) & 1;
-    const bool more = t + 1 < t_hi;
-    if (more) load_tile(t + 1);
+  auto body = [&](int t, auto stage_c) {
+    constexpr int st = decltype(stage_c)::value;
+    if (t + 1 < t_hi) issue(t + 1, std::integral_constant<int, st ^ 1>{});
+    opaque(abase);
+    opaque(tr_lo);
+    opaque(tr_hi);
     const int j0 = t * BC, j1 = j0 + BC - 1;
     const bool skip = !wave_live || (p.wr >= 0 && j0 > wq_last + p.wr) || (p.wl >= 0 && j1 < qw0 - p.wl);
     if (!skip) {
+      const char* kb = smem + st * STAGE;
+      const char* vb = kb + TILE;
+      // S^T = K Q^T and dP^T = V dO^T: rows are keys (A lane m reads row kperm(m)), columns queries.
+      f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const uint32_t ax = abase ^ (ks << 5);
+        s = mfma32(lds_read16(kb, ax), qf[ks], s);
+        dp = mfma32(lds_read16(vb, ax), of[ks], dp);
+      }
+      float pr[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float y = s[r] * p.scale_log2;
+        if (ALIBI) y = fmaf(-slope2, fabsf((float)(qi - (j0 + key_of_reg(r, hh)))), y);
+        pr[r] = fast_exp2(y - lse2);
+      }
       const bool full = j1 < N && wq_last == qw0 + 31 && (p.wr < 0 || j1 <= qw0 + p.wr) &&
                         (p.wl < 0 || j0 >= wq_last - p.wl);
-      if (full) {
-        compute(stage, j0, std::false_type{});
-      } else {
-        compute(stage, j0, std::true_type{});
+      if (!full) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = j0 + key_of_reg(r, hh);
+          const bool vis = key < N && qi < N && (p.wr < 0 || key <= qi + p.wr) && (p.wl < 0 || key >= qi - p.wl);
+          pr[r] = vis ? pr[r] : 0.f;
+        }
+      }
+      uint32_t tx_lo[MB], tx_hi[MB];
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        tx_lo[mb] = tr_lo ^ (mb << 6);
+        tx_hi[mb] = tr_hi ^ (mb << 6);
+      }
+      // dQ^T += K^T dS^T: A = K^T read transposed from the K tile, B = dS^T from registers.
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        float d8[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) d8[e] = pr[8 * kk + e] * (dp[8 * kk + e] - delta);
+        const bf16x8 dsb = pack_bf16x8(d8[0], d8[1], d8[2], d8[3], d8[4], d8[5], d8[6], d8[7]);
+        const int ro = kk * 16 * ROWB;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          const bf16x4 lo = lds_read_tr(kb + ro + tx_lo[mb]);
+          const bf16x4 hi = lds_read_tr(kb + ro + tx_hi[mb]);
+          acc[mb] = mfma32(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), dsb, acc[mb]);
+        }
       }
     }
-    if (more) store_tile(stage ^ 1);
-    __syncthreads();
+    wait_all_and_sync();
+  };
+
+  issue(t_lo, std::integral_constant<int, 0>{});
+  wait_all_and_sync();
+  for (int t = t_lo; t < t_hi; t += 2) {
+    body(t, std::integral_constant<int, 0>{});
+    if (t + 1 < t_hi) body(t + 1, std::integral_constant<int, 1>{});
   }
   if (!wave_live || qi >= N) return;
   bf16* dq_row = (bf16*)p.dq + base + (int64_t)qi * rs;

@@ -152,6 +152,31 @@ __device__ __forceinline__ void opaque(T& x) {
   asm volatile("" : "+v"(x));
 }
 
+// Workgroup id -> (head index bh, block index within the head).
+//
+// Workgroups are dispatched round-robin over the 8 XCDs (id % 8), and each XCD
+// has its own L2. When bh_count is a multiple of 8, XCD x gets the heads
+// bh = x, x+8, ...; it walks them G heads at a time, and within a group the
+// blocks run in `order` (longest first), interleaved over the G heads. So the
+// workgroups resident on one XCD share few heads and re-read the same K/V (or
+// Q/dO) tiles from their L2. Otherwise the ids map head-fastest.
+// `descending`: block index runs nblk-1 .. 0 (causal forward: long blocks are
+// the late query blocks); else 0 .. nblk-1 (causal backward: early key blocks).
+template <int G>
+__device__ __forceinline__ void grid_map(int id, int nblk, int bh_count, bool descending, int& bh, int& blk) {
+  int r;
+  if ((bh_count & 7) == 0 && ((bh_count >> 3) % G) == 0) {
+    const int xcd = id & 7, s = id >> 3;
+    const int group = s / (G * nblk), rem = s % (G * nblk);
+    r = rem / G;
+    bh = ((group * G + rem % G) << 3) + xcd;
+  } else {
+    r = id / bh_count;
+    bh = id % bh_count;
+  }
+  blk = descending ? nblk - 1 - r : r;
+}
+
 struct FwdParams {
   const void* q;
   const void* k;

@@ -3,6 +3,8 @@
 // neither the device nor the runtime.
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
 
 #include "../../include/fa2.h"
 #include "launch.hpp"
@@ -113,7 +115,16 @@ fa2_status_t fa2_bwd(const void* q, const void* k, const void* v, const void* ou
   p.causal = causal ? 1 : 0;
   p.wl = window_left;
   p.wr = causal ? 0 : window_right;
-  hipError_t e = fa2::launch_bwd_bf16(p, d, deterministic != 0, (hipStream_t)stream);
+  // The separate dQ pass (no atomics) is both bitwise repeatable and, on MI355X,
+  // faster than accumulating dQ with float atomics, so it serves both values of
+  // `deterministic`. FA2_BWD_ATOMIC_DQ=1 selects the atomic variant when
+  // determinism is not requested (a tuning switch; results stay within tolerance).
+  bool split_dq = true;
+  if (deterministic == 0) {
+    const char* env = getenv("FA2_BWD_ATOMIC_DQ");
+    if (env && strcmp(env, "1") == 0) split_dq = false;
+  }
+  hipError_t e = fa2::launch_bwd_bf16(p, d, split_dq, (hipStream_t)stream);
   if (e == hipErrorNotSupported) return FA2_ERR_UNSUPPORTED;
   return e == hipSuccess ? FA2_OK : FA2_ERR_HIP;
 }

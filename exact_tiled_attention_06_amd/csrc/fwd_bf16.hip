@@ -39,6 +39,10 @@
 namespace fa2 {
 
 constexpr float kRescaleLog2 = 8.0f;
+#ifndef FA2_HEAD_GROUP
+#define FA2_HEAD_GROUP 4
+#endif
+constexpr int kHeadGroup = FA2_HEAD_GROUP;  // heads walked together per XCD
 
 template <int D, int NW, int BC>
 struct FwdShape {
@@ -59,9 +63,8 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdParams p) {
   constexpr int PER_WAVE = S::TILE / (1024 * NW);  // 1 KB direct-load pieces per wave per tensor
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
-  const int bh_count = p.B * p.H;
-  const int qb = p.n_qblocks - 1 - (int)(blockIdx.x / bh_count);  // longest blocks first
-  const int bh = (int)(blockIdx.x % bh_count);
+  int bh, qb;
+  grid_map<kHeadGroup>((int)blockIdx.x, p.n_qblocks, p.B * p.H, true, bh, qb);  // longest blocks first
   const int b = bh / p.H, h = bh % p.H;
   const int N = p.N;
 

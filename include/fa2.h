@@ -94,9 +94,12 @@ size_t fa2_bwd_workspace_size(int B, int H, int N, int d);
  * (written). workspace: device memory of at least fa2_bwd_workspace_size()
  * bytes (workspace_bytes says how much was given; too little is
  * FA2_ERR_INVALID_ARG); its contents need not be initialised and are
- * overwritten. deterministic = 0: dQ is accumulated with float32 atomics, so
- * dq may differ in the last bits between runs; deterministic != 0: dQ is
- * computed by a separate pass without atomics and is bitwise repeatable.
+ * overwritten. deterministic != 0 guarantees bitwise-repeatable results: dQ is
+ * formed by a separate pass over query blocks, without atomics. With
+ * deterministic = 0 the library may choose; it currently uses the same pass
+ * (the faster one on MI355X). Setting the environment variable
+ * FA2_BWD_ATOMIC_DQ=1 makes deterministic = 0 accumulate dQ with float32
+ * atomics instead, in which case dq may differ in the last bits between runs.
  * No gradient is produced for the ALiBi slopes.
  */
 fa2_status_t fa2_bwd(const void* q, const void* k, const void* v, const void* out,

@@ -26,11 +26,22 @@ MASKS = {
 
 
 def run_fwd_bwd(fa2, dev, slopes, scale, causal, window, deterministic=False):
+    """deterministic: False = library default, True = deterministic flag, "atomic" =
+    the float-atomic dQ variant (FA2_BWD_ATOMIC_DQ=1 with deterministic = 0)."""
+    import os
+    atomic = deterministic == "atomic"
+    if atomic:
+        os.environ["FA2_BWD_ATOMIC_DQ"] = "1"
+        deterministic = False
     sl = None if slopes is None else slopes.cuda()
     out, lse = fa2.flash_attn_fwd(dev["q"], dev["k"], dev["v"], scale, causal, window, sl)
-    dq, dk, dv = fa2.flash_attn_bwd(dev["dout"], dev["q"], dev["k"], dev["v"], out, lse, scale, causal, window,
-                                    sl, deterministic)
-    torch.cuda.synchronize()
+    try:
+        dq, dk, dv = fa2.flash_attn_bwd(dev["dout"], dev["q"], dev["k"], dev["v"], out, lse, scale, causal, window,
+                                        sl, deterministic)
+        torch.cuda.synchronize()
+    finally:
+        if atomic:
+            del os.environ["FA2_BWD_ATOMIC_DQ"]
     return dq, dk, dv
 
 
@@ -45,7 +56,7 @@ def check_small(fa2, B, H, N, d, causal, window, alibi, deterministic, seed):
     return dq, dk, dv
 
 
-@pytest.mark.parametrize("deterministic", [False, True])
+@pytest.mark.parametrize("deterministic", [False, True, "atomic"])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("mask", sorted(MASKS))
 def test_small_bf16_gradients(gpu_lib, d, mask, deterministic):
@@ -60,7 +71,7 @@ def test_edge_lengths(gpu_lib, N):
     check_small(gpu_lib, 1, 2, N, 128, True, (-1, -1), False, False, seed=N + 100)
 
 
-@pytest.mark.parametrize("deterministic", [False, True])
+@pytest.mark.parametrize("deterministic", [False, True, "atomic"])
 def test_self_only_window_has_zero_dq_dk(gpu_lib, deterministic):
     """window (0, 0): each query sees only itself, P = 1, D = dP, so dS = 0: dQ = dK = 0 and dV = dO."""
     cpu, dev, _ = gpu_inputs(1, 2, 190, 128, "bf16", seed=43, with_dout=True)
@@ -69,10 +80,11 @@ def test_self_only_window_has_zero_dq_dk(gpu_lib, deterministic):
     assert torch.equal(dv.cpu(), cpu["dout"])
 
 
-def test_deterministic_mode_is_bitwise_repeatable(gpu_lib):
+@pytest.mark.parametrize("deterministic", [False, True])
+def test_bitwise_repeatable(gpu_lib, deterministic):
     cpu, dev, slopes = gpu_inputs(1, 4, 700, 128, "bf16", seed=41, with_dout=True, alibi=True)
-    a = run_fwd_bwd(gpu_lib, dev, slopes, scale_of(128), True, (200, 0), deterministic=True)
-    b = run_fwd_bwd(gpu_lib, dev, slopes, scale_of(128), True, (200, 0), deterministic=True)
+    a = run_fwd_bwd(gpu_lib, dev, slopes, scale_of(128), True, (200, 0), deterministic=deterministic)
+    b = run_fwd_bwd(gpu_lib, dev, slopes, scale_of(128), True, (200, 0), deterministic=deterministic)
     for x, y in zip(a, b):
         assert torch.equal(x, y)
 
@@ -86,7 +98,7 @@ def test_dv_columns_sum_to_dout_columns(gpu_lib):
     assert np.max(np.abs(lhs - rhs)) / np.max(np.abs(rhs)) < 2e-2
 
 
-@pytest.mark.parametrize("deterministic", [False, True])
+@pytest.mark.parametrize("deterministic", [False, "atomic"])
 @pytest.mark.parametrize("number", [4, 5])
 def test_full_size_workload_sampled_rows(gpu_lib, number, deterministic):
     w = workloads.WORKLOADS[number]

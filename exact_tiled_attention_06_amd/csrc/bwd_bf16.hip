@@ -38,9 +38,10 @@ namespace fa2 {
 #endif
 constexpr int kHeadGroup = FA2_HEAD_GROUP;  // heads walked together per XCD
 
-template <int D>
+template <int D, int NW_, int NST_, bool DET_>
 struct BwdShape {
-  static constexpr int NW = 4;
+  static constexpr int NW = NW_;
+  static constexpr int NST = NST_;
   static constexpr int NT = NW * 64;
   static constexpr int BK = NW * 32;                    // keys per workgroup
   static constexpr int BQ = 32;                         // queries per iteration
@@ -50,12 +51,12 @@ struct BwdShape {
   static constexpr int K_BYTES = BK * D * 2;            // resident K tile
   static constexpr int QT_BYTES = BQ * D * 2;           // one Q or dO tile
   static constexpr int STAGE_BYTES = 2 * QT_BYTES + 2 * BQ * 4;
-  static constexpr int DS_BYTES = BK * BQ * 2;          // dS^T, [key][query]
-  static constexpr int LDS = K_BYTES + 2 * STAGE_BYTES + DS_BYTES;
-  static constexpr int QCPT = BQ * CPR / NT;            // Q chunks per thread
-  static constexpr int KCPT = BK * CPR / NT;            // K chunks per thread
+  static constexpr int DS_BYTES = DET_ ? 0 : BK * BQ * 2;  // dS^T, [key][query]
+  static constexpr int LDS = K_BYTES + NST * STAGE_BYTES + DS_BYTES;
   static constexpr int DQ_SPLIT = NW / MB;              // waves per d-block in the dQ step
-  static_assert(BQ * CPR % NT == 0 && BK * CPR % NT == 0, "even split");
+  static constexpr int PER_WAVE = QT_BYTES / (1024 * NW);  // 1 KB direct-load pieces per wave per tile
+  static_assert(QT_BYTES % (1024 * NW) == 0, "Q tile must split into 1 KB pieces per wave");
+  static_assert(LDS <= 160 * 1024, "LDS budget");
 };
 
 // dS^T tile: rows of 32 queries (64 bytes); chunk c of key row r at c ^ ((r/4)%4).
@@ -114,9 +115,9 @@ __global__ __launch_bounds__(256) void bwd_dq_convert_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------- pass 2
-template <int D, bool ALIBI, bool DET>
-__global__ __launch_bounds__(256, (D == 128 && !DET) ? 1 : 2) void bwd_main_kernel(BwdParams p) {
-  using S = BwdShape<D>;
+template <int D, bool ALIBI, bool DET, int NW, int NST>
+__global__ __launch_bounds__(NW * 64, ((D == 128 && !DET) ? 4 : 8) / NW) void bwd_main_kernel(BwdParams p) {
+  using S = BwdShape<D, NW, NST, DET>;
   constexpr int ROWB = 2 * D;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   char* k_lds = smem;
@@ -150,7 +151,7 @@ __global__ __launch_bounds__(256, (D == 128 && !DET) ? 1 : 2) void bwd_main_kern
   for (int ks = 0; ks < S::KS; ++ks)
     vf[ks] = kj < N ? *reinterpret_cast<const bf16x8*>(vg + (int64_t)kj * rs + 16 * ks + 8 * hh) : bf16x8{};
   // Resident K tile (B operand of S, and K of dQ = dS K).
-  dma_tile<D, S::BK, S::NW>(k_lds, kg, rs, k0, N, w, lane);
+  dma_tile<D, S::BK, NW>(k_lds, kg, rs, k0, N, w, lane);
 
   const float slope2 = ALIBI ? p.alibi[h] * kLog2e : 0.f;
 
@@ -186,7 +187,7 @@ __global__ __launch_bounds__(256, (D == 128 && !DET) ? 1 : 2) void bwd_main_kern
   }
 
   // Per-lane byte offsets of this lane's direct-load pieces of a Q/dO tile.
-  constexpr int PER_WAVE = S::QT_BYTES / (1024 * S::NW);
+  constexpr int PER_WAVE = S::PER_WAVE;
   uint32_t dma_off[PER_WAVE];
 #pragma unroll
   for (int n = 0; n < PER_WAVE; ++n) {
@@ -197,7 +198,7 @@ __global__ __launch_bounds__(256, (D == 128 && !DET) ? 1 : 2) void bwd_main_kern
   }
 
   // Q, dO (swizzled tiles) and LSE, D (raw floats) of query block `it` into a stage.
-  auto issue_q = [&](int it, auto stage_c) {
+  auto issue_q = [&](int it, auto stage_c) __attribute__((always_inline)) {
     constexpr int stg = decltype(stage_c)::value;
     char* st = stage_lds + stg * S::STAGE_BYTES;
     const int i0 = it * S::BQ;
@@ -222,10 +223,20 @@ __global__ __launch_bounds__(256, (D == 128 && !DET) ? 1 : 2) void bwd_main_kern
     }
   };
 
+  // Query block it + 1 must have landed; NST - 2 younger blocks may still be in
+  // flight (wave 0 issues one extra load per block, for LSE and D).
+  auto wait_next = [&]() __attribute__((always_inline)) {
+    if (w == 0) {
+      wait_vm_and_sync<(2 * PER_WAVE + 1) * (NST - 2)>();
+    } else {
+      wait_vm_and_sync<2 * PER_WAVE * (NST - 2)>();
+    }
+  };
+
   // One 32-query block; the stage is a compile-time constant.
-  auto body = [&](int it, auto stage_c) {
+  auto body = [&](int it, auto stage_c) __attribute__((always_inline)) {
     constexpr int stg = decltype(stage_c)::value;
-    if (it + 1 < it_hi) issue_q(it + 1, std::integral_constant<int, stg ^ 1>{});
+    if (it + NST - 1 < it_hi) issue_q(it + NST - 1, std::integral_constant<int, (stg + NST - 1) % NST>{});
     opaque(qa_base);
     opaque(kb_base);
     opaque(tr_lo);
@@ -343,14 +354,19 @@ __global__ __launch_bounds__(256, (D == 128 && !DET) ? 1 : 2) void bwd_main_kern
         if (i0 + m < N) atomicAdd(dq_row + (int64_t)m * D, dqa[r]);
       }
     }
-    wait_all_and_sync();
+    wait_next();
   };
 
-  issue_q(it_lo, std::integral_constant<int, 0>{});
-  wait_all_and_sync();
-  for (int it = it_lo; it < it_hi; it += 2) {
-    body(it, std::integral_constant<int, 0>{});
-    if (it + 1 < it_hi) body(it + 1, std::integral_constant<int, 1>{});
+  static_for<0, NST - 1>([&](auto sc) {
+    constexpr int k = decltype(sc)::value;
+    if (it_lo + k < it_hi) issue_q(it_lo + k, std::integral_constant<int, k>{});
+  });
+  wait_next();
+  for (int it = it_lo; it < it_hi; it += NST) {
+    static_for<0, NST>([&](auto sc) {
+      constexpr int k = decltype(sc)::value;
+      if (it + k < it_hi) body(it + k, sc);
+    });
   }
 
   // dK = scale * dK^T, dV = dV^T, stored as bf16: lane holds key kj, d = 32*mb + 8*a + 4*hh + (0..3).
@@ -380,14 +396,15 @@ __global__ __launch_bounds__(256, (D == 128 && !DET) ? 1 : 2) void bwd_main_kern
 // dP^T = V dO^T put one query per lane (column), so LSE and D are per-lane
 // scalars, and dS^T feeds dQ^T += K^T dS^T as the B operand straight from
 // registers (K^T read transposed from the K tile).
-template <int D, bool ALIBI>
-__global__ __launch_bounds__(256, 2) void bwd_dq_det_kernel(BwdParams p) {
-  constexpr int NW = 4, BR = NW * 32, BC = 32;
+template <int D, bool ALIBI, int NW, int NST>
+__global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq_det_kernel(BwdParams p) {
+  constexpr int BR = NW * 32, BC = 32;
   constexpr int KS = D / 16, MB = D / 32;
   constexpr int ROWB = 2 * D;
   constexpr int TILE = BC * D * 2;
   constexpr int STAGE = 2 * TILE;
   constexpr int PER_WAVE = TILE / (1024 * NW);
+  static_assert(TILE % (1024 * NW) == 0, "tile must split into 1 KB pieces per wave");
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
   int bh, qb;
@@ -446,7 +463,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_det_kernel(BwdParams p) {
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) acc[mb] = f32x16{};
 
-  auto issue = [&](int t, auto stage_c) {
+  auto issue = [&](int t, auto stage_c) __attribute__((always_inline)) {
     constexpr int st = decltype(stage_c)::value;
     char* kl = smem + st * STAGE;
     const int row0 = t * BC;
@@ -466,9 +483,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_det_kernel(BwdParams p) {
     }
   };
 
-  auto body = [&](int t, auto stage_c) {
+  auto body = [&](int t, auto stage_c) __attribute__((always_inline)) {
     constexpr int st = decltype(stage_c)::value;
-    if (t + 1 < t_hi) issue(t + 1, std::integral_constant<int, st ^ 1>{});
+    if (t + NST - 1 < t_hi) issue(t + NST - 1, std::integral_constant<int, (st + NST - 1) % NST>{});
     opaque(abase);
     opaque(tr_lo);
     opaque(tr_hi);
@@ -524,14 +541,19 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_det_kernel(BwdParams p) {
         }
       }
     }
-    wait_all_and_sync();
+    wait_vm_and_sync<2 * PER_WAVE * (NST - 2)>();  // tile t + 1 has landed
   };
 
-  issue(t_lo, std::integral_constant<int, 0>{});
-  wait_all_and_sync();
-  for (int t = t_lo; t < t_hi; t += 2) {
-    body(t, std::integral_constant<int, 0>{});
-    if (t + 1 < t_hi) body(t + 1, std::integral_constant<int, 1>{});
+  static_for<0, NST - 1>([&](auto sc) {
+    constexpr int k = decltype(sc)::value;
+    if (t_lo + k < t_hi) issue(t_lo + k, std::integral_constant<int, k>{});
+  });
+  wait_vm_and_sync<2 * PER_WAVE * (NST - 2)>();
+  for (int t = t_lo; t < t_hi; t += NST) {
+    static_for<0, NST>([&](auto sc) {
+      constexpr int k = decltype(sc)::value;
+      if (t + k < t_hi) body(t + k, sc);
+    });
   }
   if (!wave_live || qi >= N) return;
   bf16* dq_row = (bf16*)p.dq + base + (int64_t)qi * rs;
@@ -548,6 +570,19 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_det_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------- launch
+#ifndef FA2_BWD_NW
+#define FA2_BWD_NW 8
+#endif
+#ifndef FA2_BWD_NST
+#define FA2_BWD_NST 4
+#endif
+#ifndef FA2_DQ_NW
+#define FA2_DQ_NW 4
+#endif
+#ifndef FA2_DQ_NST
+#define FA2_DQ_NST 3
+#endif
+
 template <typename K>
 static hipError_t set_lds(K kern, int bytes) {
   return hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
@@ -555,7 +590,11 @@ static hipError_t set_lds(K kern, int bytes) {
 
 template <int D, bool ALIBI, bool DET>
 static hipError_t launch_bwd_cfg(const BwdParams& p, hipStream_t stream) {
-  using S = BwdShape<D>;
+  // Split dQ pass (DET): deeper Q/dO ring and 8 waves per key block; atomic dQ:
+  // 4 waves, 2 stages (its dS^T buffer and dQ step need the room).
+  constexpr int NW = DET ? (D == 128 ? FA2_BWD_NW : 4) : 4;
+  constexpr int NST = DET ? (D == 128 ? FA2_BWD_NST : 3) : 2;
+  using S = BwdShape<D, NW, NST, DET>;
   const int64_t rows = (int64_t)p.B * p.N * p.H;
   constexpr int RPB = 256 / (D / 8);
   const unsigned row_blocks = (unsigned)((rows + RPB - 1) / RPB);
@@ -563,7 +602,7 @@ static hipError_t launch_bwd_cfg(const BwdParams& p, hipStream_t stream) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 
-  auto kmain = bwd_main_kernel<D, ALIBI, DET>;
+  auto kmain = bwd_main_kernel<D, ALIBI, DET, NW, NST>;
   static bool main_attr = false;
   if (!main_attr) {
     if ((e = set_lds(kmain, S::LDS)) != hipSuccess) return e;
@@ -574,15 +613,17 @@ static hipError_t launch_bwd_cfg(const BwdParams& p, hipStream_t stream) {
   if ((e = hipGetLastError()) != hipSuccess) return e;
 
   if (DET) {
-    auto kdq = bwd_dq_det_kernel<D, ALIBI>;
-    constexpr int DQ_LDS = 2 * 2 * 32 * D * 2;
+    constexpr int DNW = D == 128 ? FA2_DQ_NW : 4;
+    constexpr int DNST = FA2_DQ_NST;
+    auto kdq = bwd_dq_det_kernel<D, ALIBI, DNW, DNST>;
+    constexpr int DQ_LDS = DNST * 2 * 32 * D * 2;
     static bool dq_attr = false;
     if (!dq_attr) {
       if ((e = set_lds(kdq, DQ_LDS)) != hipSuccess) return e;
       dq_attr = true;
     }
-    const int nqb = (p.N + 127) / 128;
-    hipLaunchKernelGGL(kdq, dim3((unsigned)((int64_t)nqb * p.B * p.H)), dim3(256), DQ_LDS, stream, p);
+    const int nqb = (p.N + DNW * 32 - 1) / (DNW * 32);
+    hipLaunchKernelGGL(kdq, dim3((unsigned)((int64_t)nqb * p.B * p.H)), dim3(DNW * 64), DQ_LDS, stream, p);
   } else {
     hipLaunchKernelGGL(bwd_dq_convert_kernel<D>, dim3(row_blocks), dim3(256), 0, stream, p);
   }

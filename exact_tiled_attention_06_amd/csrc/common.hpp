@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace fa2 {
 
 typedef __bf16 bf16;
@@ -142,6 +144,25 @@ __device__ __forceinline__ void dma_tile(char* lds_tile, const bf16* g, int64_t 
 __device__ __forceinline__ void wait_all_and_sync() {
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+}
+
+// Wait until at most N vector-memory operations of this wave are outstanding
+// (direct global->LDS loads included; they complete in issue order) and all LDS
+// operations are done, then synchronise the workgroup.
+template <int N>
+__device__ __forceinline__ void wait_vm_and_sync() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  // s_waitcnt: vmcnt[3:0] | expcnt[6:4] (7 = no wait) | lgkmcnt[11:8] | vmcnt[5:4] at [15:14]
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | ((N >> 4) << 14));
+  __syncthreads();
+}
+
+template <int I, int N, typename F>
+__device__ __attribute__((always_inline)) inline void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
 }
 
 // Hides a value from the optimiser so that expressions built from it are

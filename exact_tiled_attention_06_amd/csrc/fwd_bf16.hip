@@ -44,7 +44,7 @@ constexpr float kRescaleLog2 = 8.0f;
 #endif
 constexpr int kHeadGroup = FA2_HEAD_GROUP;  // heads walked together per XCD
 
-template <int D, int NW, int BC>
+template <int D, int NW, int BC, int NST>
 struct FwdShape {
   static constexpr int NT = NW * 64;        // threads
   static constexpr int BR = NW * 32;        // query rows per workgroup
@@ -53,14 +53,16 @@ struct FwdShape {
   static constexpr int KS = D / 16;         // MFMA reduction steps over d
   static constexpr int MB = D / 32;         // 32-row blocks of O^T
   static constexpr int STAGE = 2 * TILE;    // K and V of one tile
-  static constexpr int LDS = 2 * STAGE;     // two stages
+  static constexpr int LDS = NST * STAGE;   // NST-stage ring: NST - 1 tiles in flight
+  static constexpr int PER_WAVE = TILE / (1024 * NW);  // 1 KB direct-load pieces per wave per tensor
+  static constexpr int VM_PER_TILE = 2 * PER_WAVE;     // direct loads per wave per tile (K and V)
   static constexpr int ROWB = 2 * D;        // bytes per LDS row
 };
 
-template <int D, int NW, int BC, bool ALIBI>
-__global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdParams p) {
-  using S = FwdShape<D, NW, BC>;
-  constexpr int PER_WAVE = S::TILE / (1024 * NW);  // 1 KB direct-load pieces per wave per tensor
+template <int D, int NW, int BC, int NST, bool ALIBI>
+__global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(FwdParams p) {
+  using S = FwdShape<D, NW, BC, NST>;
+  constexpr int PER_WAVE = S::PER_WAVE;
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
   int bh, qb;
@@ -126,7 +128,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdParams p) {
   float m2 = kNoMax;                   // running max, log2 units
   float lsum[4] = {0.f, 0.f, 0.f, 0.f};  // running sum (this lane half's keys), 4 partial sums
 
-  auto issue = [&](int t, auto stage_c) {
+  auto issue = [&](int t, auto stage_c) __attribute__((always_inline)) {
     constexpr int st = decltype(stage_c)::value;
     char* kl = smem + st * S::STAGE;
     const int row0 = t * BC;
@@ -147,9 +149,10 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdParams p) {
   };
 
   // One tile of the online softmax for this wave; the stage is a compile-time constant.
-  auto body = [&](int t, auto stage_c) {
+  // Tile t + NST - 1 is issued into the stage freed by tile t - 1.
+  auto body = [&](int t, auto stage_c) __attribute__((always_inline)) {
     constexpr int st = decltype(stage_c)::value;
-    if (t + 1 < t_hi) issue(t + 1, std::integral_constant<int, st ^ 1>{});
+    if (t + NST - 1 < t_hi) issue(t + NST - 1, std::integral_constant<int, (st + NST - 1) % NST>{});
     opaque(kbase);
     opaque(vbase_lo);
     opaque(vbase_hi);
@@ -246,14 +249,20 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdParams p) {
         }
       }
     }
-    wait_all_and_sync();
+    // Tile t + 1 must have landed; the NST - 2 younger tiles may still be in flight.
+    wait_vm_and_sync<S::VM_PER_TILE * (NST - 2)>();
   };
 
-  issue(t_lo, std::integral_constant<int, 0>{});
-  wait_all_and_sync();
-  for (int t = t_lo; t < t_hi; t += 2) {
-    body(t, std::integral_constant<int, 0>{});
-    if (t + 1 < t_hi) body(t + 1, std::integral_constant<int, 1>{});
+  static_for<0, NST - 1>([&](auto sc) {
+    constexpr int k = decltype(sc)::value;
+    if (t_lo + k < t_hi) issue(t_lo + k, std::integral_constant<int, k>{});
+  });
+  wait_vm_and_sync<S::VM_PER_TILE * (NST - 2)>();
+  for (int t = t_lo; t < t_hi; t += NST) {
+    static_for<0, NST>([&](auto sc) {
+      constexpr int k = decltype(sc)::value;
+      if (t + k < t_hi) body(t + k, sc);
+    });
   }
 
   if (!wave_live) return;
@@ -277,12 +286,12 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdParams p) {
   }
 }
 
-template <int D, int NW, int BC, bool ALIBI>
+template <int D, int NW, int BC, int NST, bool ALIBI>
 static hipError_t launch_fwd_cfg(const FwdParams& p0, hipStream_t stream) {
-  using S = FwdShape<D, NW, BC>;
+  using S = FwdShape<D, NW, BC, NST>;
   FwdParams p = p0;
   p.n_qblocks = (p.N + S::BR - 1) / S::BR;
-  auto kern = fwd_bf16_kernel<D, NW, BC, ALIBI>;
+  auto kern = fwd_bf16_kernel<D, NW, BC, NST, ALIBI>;
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, S::LDS);
@@ -294,18 +303,21 @@ static hipError_t launch_fwd_cfg(const FwdParams& p0, hipStream_t stream) {
   return hipGetLastError();
 }
 
-int64_t fwd_bf16_grid_blocks(int B, int H, int N, int d) {
-  (void)d;
-  const int BR = 4 * 32;
-  return (int64_t)((N + BR - 1) / BR) * B * H;
-}
+#ifndef FA2_FWD_NW
+#define FA2_FWD_NW 4
+#endif
+#ifndef FA2_FWD_NST
+#define FA2_FWD_NST 2
+#endif
 
 hipError_t launch_fwd_bf16(const FwdParams& p, int d, hipStream_t stream) {
+  constexpr int NW = FA2_FWD_NW, NST = FA2_FWD_NST;
   const bool alibi = p.alibi != nullptr;
   if (d == 128) {
-    return alibi ? launch_fwd_cfg<128, 4, 64, true>(p, stream) : launch_fwd_cfg<128, 4, 64, false>(p, stream);
+    return alibi ? launch_fwd_cfg<128, NW, 64, NST, true>(p, stream)
+                 : launch_fwd_cfg<128, NW, 64, NST, false>(p, stream);
   }
-  return alibi ? launch_fwd_cfg<64, 4, 64, true>(p, stream) : launch_fwd_cfg<64, 4, 64, false>(p, stream);
+  return alibi ? launch_fwd_cfg<64, NW, 64, NST, true>(p, stream) : launch_fwd_cfg<64, NW, 64, NST, false>(p, stream);
 }
 
 }  // namespace fa2

@@ -64,13 +64,34 @@ def cpu_baseline(w, min_seconds=10.0, max_heads=16):
     }
 
 
+def recorded_traffic(call):
+    """HBM bytes per launch of the dominant kernel from the committed rocprofv3
+    FETCH_SIZE / WRITE_SIZE passes (profiles/hbm_traffic.json), reported only if
+    the kernel sources still hash to the values the counters were taken with."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    ent = rec.get("kernels", {}).get(call)
+    if not ent:
+        return None
+    h = hashlib.sha256()
+    for f in rec["sources"]:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    if h.hexdigest() != rec["sources_sha256"]:
+        return None
+    return ent["hbm_bytes_per_launch"]
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--deterministic", action="store_true")
+    ap.add_argument("--atomic-dq", action="store_true",
+                    help="time the float-atomic dQ variant of the backward instead of the default passes")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (3 launches), used to "
                          "calibrate the FETCH_SIZE / WRITE_SIZE counters against a known byte count")
@@ -110,58 +131,79 @@ def main():
     scale = w.scale
     stream = torch.cuda.current_stream()
     sp = stream.cuda_stream
-    det = int(args.deterministic)
 
     def fwd():
         fa2.fa2_fwd(q, k, v, out, lse, B, H, N, d, scale, 1, -1, -1, None, sp)
 
-    def bwd():
-        fa2.fa2_bwd(q, k, v, out, lse, do, dq, dk, dv, ws, ws_bytes, B, H, N, d, scale, 1, -1, -1, None, det, sp)
+    # The backward as its three passes (exactly what fa2_bwd runs by default), so
+    # each kernel's duration is measured with its own events.
+    def prep():
+        fa2.fa2_bwd_prep(out, do, ws, ws_bytes, B, H, N, d, sp)
+
+    def dkdv():
+        fa2.fa2_bwd_dkdv(q, k, v, lse, do, dk, dv, ws, ws_bytes, B, H, N, d, scale, 1, -1, -1, None, sp)
+
+    def dqp():
+        fa2.fa2_bwd_dq(q, k, v, lse, do, dq, ws, ws_bytes, B, H, N, d, scale, 1, -1, -1, None, sp)
+
+    def bwd_atomic():
+        fa2.fa2_bwd(q, k, v, out, lse, do, dq, dk, dv, ws, ws_bytes, B, H, N, d, scale, 1, -1, -1, None, 0, sp)
+
+    phases = [("fwd", fwd), ("bwd_prep", prep), ("bwd_dkdv", dkdv), ("bwd_dq", dqp)]
+    if args.atomic_dq:
+        os.environ["FA2_BWD_ATOMIC_DQ"] = "1"
+        phases = [("fwd", fwd), ("bwd_atomic", bwd_atomic)]
 
     for _ in range(args.warmup):
-        fwd()
-        bwd()
+        for _, fn in phases:
+            fn()
     torch.cuda.synchronize()
 
     K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(phases) + 1)] for _ in range(K)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start.record(stream)
     for i in range(K):
         ev[i][0].record(stream)
-        fwd()
-        ev[i][1].record(stream)
-        bwd()
-        ev[i][2].record(stream)
+        for n, (_, fn) in enumerate(phases):
+            fn()
+            ev[i][n + 1].record(stream)
     t_end.record(stream)
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
-    fwd_ms = sorted(e[0].elapsed_time(e[1]) for e in ev)
-    bwd_ms = sorted(e[1].elapsed_time(e[2]) for e in ev)
     ms_step = total_ms / K
+    ph_ms = {name: sum(e[n].elapsed_time(e[n + 1]) for e in ev) / K for n, (name, _) in enumerate(phases)}
     f_fwd, f_bwd = flops(B, H, N, d, True)
-    fwd_avg = sum(fwd_ms) / K
-    bwd_avg = sum(bwd_ms) / K
+    pairs = B * H * N * (N + 1) / 2  # visible (query, key) pairs, causal
+    fwd_avg = ph_ms["fwd"]
+    bwd_avg = sum(v for kk, v in ph_ms.items() if kk != "fwd")
     fwd_tf = f_fwd / (fwd_avg * 1e-3) / 1e12
     bwd_tf = f_bwd / (bwd_avg * 1e-3) / 1e12
     value = (f_fwd + f_bwd) / (ms_step * 1e-3) / 1e12
 
-    kernels = {
-        "fa2_fwd": {"kernel": "fwd_bf16_kernel<128,4,64>", "bound": "mfma", "achieved": round(fwd_tf, 2),
-                    "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(fwd_tf / PEAK_BF16_TFLOPS, 4),
-                    "avg_ms": round(fwd_avg, 4), "median_ms": round(fwd_ms[K // 2], 4),
-                    "flop_per_launch": f_fwd},
-        "fa2_bwd": {"kernel": "bwd_main_kernel<128> (+ delta and dQ-convert passes in the same call)",
-                    "bound": "mfma", "achieved": round(bwd_tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                    "frac": round(bwd_tf / PEAK_BF16_TFLOPS, 4), "avg_ms": round(bwd_avg, 4),
-                    "median_ms": round(bwd_ms[K // 2], 4), "flop_per_launch": f_bwd},
+    # Per-kernel rooflines. Executed MFMA FLOPs per launch: forward 4*d per visible
+    # pair (S, P V); dK/dV pass 8*d (S, dP, dV, dK); dQ pass 6*d (S, dP, dQ).
+    kinfo = {
+        "fwd": ("fwd_bf16_kernel", 4 * d * pairs),
+        "bwd_dkdv": ("bwd_main_kernel (dK, dV)", 8 * d * pairs),
+        "bwd_dq": ("bwd_dq_det_kernel (dQ)", 6 * d * pairs),
     }
-    dom = "fa2_bwd" if bwd_avg >= fwd_avg else "fa2_fwd"
+    kernels = {}
+    for name, ms in ph_ms.items():
+        ent = {"avg_ms": round(ms, 4)}
+        if name in kinfo:
+            kn, fl = kinfo[name]
+            ach = fl / (ms * 1e-3) / 1e12
+            ent.update({"kernel": kn, "bound": "mfma", "flop_per_launch": fl, "achieved": round(ach, 2),
+                        "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4)})
+        kernels[name] = ent
+    dom = max((n for n in kernels if "frac" in kernels[n]), key=lambda n: kernels[n]["avg_ms"])
     dk_ = kernels[dom]
+    traffic = recorded_traffic(dom)
     roofline = {"bound": "mfma", "achieved": dk_["achieved"], "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": dk_["frac"], "traffic": None, "kernel": dk_["kernel"], "call": dom}
+                "frac": dk_["frac"], "traffic": traffic, "kernel": dk_["kernel"], "call": dom}
 
     rec = {
         "metric": METRIC,
@@ -178,10 +220,12 @@ def main():
         "data": "synthetic",
         "config": {"workload": "bf16 causal attention fwd+bwd, B=4 H=32 N=8192 d=128 [B,N,H,d]",
                    "B": B, "H": H, "N": N, "d": d, "causal": True, "seq_len": N, "global_batch": B,
-                   "parallelism": "none (1 GPU)", "deterministic_bwd": bool(det)},
+                   "parallelism": "none (1 GPU)",
+                   "bwd_dq": "float atomics" if args.atomic_dq else "separate pass (no atomics)"},
         "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4),
         "fwd_tflops": round(fwd_tf, 2),
         "bwd_tflops": round(bwd_tf, 2),
+        "fwd_frac_of_peak": round(fwd_tf / PEAK_BF16_TFLOPS, 4),
         "roofline": roofline,
         "kernels": kernels,
     }

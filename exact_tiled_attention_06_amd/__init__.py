@@ -6,7 +6,8 @@ memory and the current stream. If the library has not been built, every call
 raises FA2Error; there is no fallback path.
 
 Low-level functions carry the C names and arguments (fa2_fwd, fa2_fwd_f32,
-fa2_bwd, fa2_bwd_workspace_size, fa2_status_string, fa2_version); tensors or
+fa2_bwd, fa2_bwd_workspace_size, fa2_bwd_prep, fa2_bwd_dkdv, fa2_bwd_dq,
+fa2_status_string, fa2_version); tensors or
 raw device addresses (int) are accepted for pointers. The convenience
 functions ``flash_attn_fwd`` / ``flash_attn_bwd`` mirror the parameter list of
 the FlashAttention v2 API on the wmrh.cn article (section 5.1) minus dropout:
@@ -21,7 +22,7 @@ import os
 
 __all__ = [
     "FA2Error", "LIB_PATH", "load_library", "fa2_fwd", "fa2_fwd_f32", "fa2_bwd",
-    "fa2_bwd_workspace_size", "fa2_status_string", "fa2_version", "flash_attn_fwd",
+    "fa2_bwd_workspace_size", "fa2_bwd_prep", "fa2_bwd_dkdv", "fa2_bwd_dq", "fa2_status_string", "fa2_version", "flash_attn_fwd",
     "flash_attn_bwd", "FA2_OK", "FA2_ERR_INVALID_ARG", "FA2_ERR_UNSUPPORTED", "FA2_ERR_HIP",
 ]
 
@@ -45,6 +46,9 @@ SIGNATURES = {
     "fa2_bwd_workspace_size": ([_I, _I, _I, _I], ctypes.c_size_t),
     "fa2_bwd": ([_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _I, _I, _I, _I, _F, _I, _I, _I,
                  _P, _I, _P], _I),
+    "fa2_bwd_prep": ([_P, _P, _P, ctypes.c_size_t, _I, _I, _I, _I, _P], _I),
+    "fa2_bwd_dkdv": ([_P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _I, _I, _I, _I, _F, _I, _I, _I, _P, _P], _I),
+    "fa2_bwd_dq": ([_P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _I, _I, _I, _I, _F, _I, _I, _I, _P, _P], _I),
     "fa2_status_string": ([_I], ctypes.c_char_p),
     "fa2_version": ([], _I),
 }
@@ -133,6 +137,30 @@ def fa2_bwd(q, k, v, out, lse, dout, dq, dk, dv, workspace, workspace_bytes, B, 
                                 int(window_right), _ptr(alibi_slopes), int(deterministic),
                                 _stream(stream))
     _check(st, "fa2_bwd")
+
+
+def fa2_bwd_prep(out, dout, workspace, workspace_bytes, B, H, N, d, stream=None):
+    st = load_library().fa2_bwd_prep(_ptr(out), _ptr(dout), _ptr(workspace), int(workspace_bytes), int(B), int(H),
+                                     int(N), int(d), _stream(stream))
+    _check(st, "fa2_bwd_prep")
+
+
+def fa2_bwd_dkdv(q, k, v, lse, dout, dk, dv, workspace, workspace_bytes, B, H, N, d, softmax_scale, causal,
+                 window_left, window_right, alibi_slopes=None, stream=None):
+    st = load_library().fa2_bwd_dkdv(_ptr(q), _ptr(k), _ptr(v), _ptr(lse), _ptr(dout), _ptr(dk), _ptr(dv),
+                                     _ptr(workspace), int(workspace_bytes), int(B), int(H), int(N), int(d),
+                                     float(softmax_scale), int(causal), int(window_left), int(window_right),
+                                     _ptr(alibi_slopes), _stream(stream))
+    _check(st, "fa2_bwd_dkdv")
+
+
+def fa2_bwd_dq(q, k, v, lse, dout, dq, workspace, workspace_bytes, B, H, N, d, softmax_scale, causal,
+               window_left, window_right, alibi_slopes=None, stream=None):
+    st = load_library().fa2_bwd_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(workspace),
+                                   int(workspace_bytes), int(B), int(H), int(N), int(d), float(softmax_scale),
+                                   int(causal), int(window_left), int(window_right), _ptr(alibi_slopes),
+                                   _stream(stream))
+    _check(st, "fa2_bwd_dq")
 
 
 # ------------------------------------------------------------------ convenience wrappers

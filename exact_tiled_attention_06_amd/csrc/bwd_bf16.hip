@@ -588,58 +588,95 @@ static hipError_t set_lds(K kern, int bytes) {
   return hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
 }
 
+// Pass 1: D = rowsum(dO * O); with zero_acc also clears the float32 dQ accumulator.
+template <int D>
+static hipError_t launch_prep_d(const BwdParams& p, bool zero_acc, hipStream_t stream) {
+  const int64_t rows = (int64_t)p.B * p.N * p.H;
+  constexpr int RPB = 256 / (D / 8);
+  const unsigned row_blocks = (unsigned)((rows + RPB - 1) / RPB);
+  hipLaunchKernelGGL(bwd_pre_kernel<D>, dim3(row_blocks), dim3(256), 0, stream, p, zero_acc ? 1 : 0);
+  return hipGetLastError();
+}
+
+// Pass 2: the key-block pass (dK, dV; with DET = false also the atomic dQ).
 template <int D, bool ALIBI, bool DET>
-static hipError_t launch_bwd_cfg(const BwdParams& p, hipStream_t stream) {
+static hipError_t launch_main_d(const BwdParams& p, hipStream_t stream) {
   // Split dQ pass (DET): deeper Q/dO ring and 8 waves per key block; atomic dQ:
   // 4 waves, 2 stages (its dS^T buffer and dQ step need the room).
   constexpr int NW = DET ? (D == 128 ? FA2_BWD_NW : 4) : 4;
   constexpr int NST = DET ? (D == 128 ? FA2_BWD_NST : 3) : 2;
   using S = BwdShape<D, NW, NST, DET>;
-  const int64_t rows = (int64_t)p.B * p.N * p.H;
-  constexpr int RPB = 256 / (D / 8);
-  const unsigned row_blocks = (unsigned)((rows + RPB - 1) / RPB);
-  hipLaunchKernelGGL(bwd_pre_kernel<D>, dim3(row_blocks), dim3(256), 0, stream, p, DET ? 0 : 1);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-
   auto kmain = bwd_main_kernel<D, ALIBI, DET, NW, NST>;
   static bool main_attr = false;
+  hipError_t e;
   if (!main_attr) {
     if ((e = set_lds(kmain, S::LDS)) != hipSuccess) return e;
     main_attr = true;
   }
   const int nkb = (p.N + S::BK - 1) / S::BK;
   hipLaunchKernelGGL(kmain, dim3((unsigned)((int64_t)nkb * p.B * p.H)), dim3(S::NT), S::LDS, stream, p);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-
-  if (DET) {
-    constexpr int DNW = D == 128 ? FA2_DQ_NW : 4;
-    constexpr int DNST = FA2_DQ_NST;
-    auto kdq = bwd_dq_det_kernel<D, ALIBI, DNW, DNST>;
-    constexpr int DQ_LDS = DNST * 2 * 32 * D * 2;
-    static bool dq_attr = false;
-    if (!dq_attr) {
-      if ((e = set_lds(kdq, DQ_LDS)) != hipSuccess) return e;
-      dq_attr = true;
-    }
-    const int nqb = (p.N + DNW * 32 - 1) / (DNW * 32);
-    hipLaunchKernelGGL(kdq, dim3((unsigned)((int64_t)nqb * p.B * p.H)), dim3(DNW * 64), DQ_LDS, stream, p);
-  } else {
-    hipLaunchKernelGGL(bwd_dq_convert_kernel<D>, dim3(row_blocks), dim3(256), 0, stream, p);
-  }
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_bf16(const BwdParams& p, int d, bool deterministic, hipStream_t stream) {
+// Pass 3 of the split backward: dQ by a sweep over key tiles per query block.
+template <int D, bool ALIBI>
+static hipError_t launch_dq_d(const BwdParams& p, hipStream_t stream) {
+  constexpr int DNW = D == 128 ? FA2_DQ_NW : 4;
+  constexpr int DNST = FA2_DQ_NST;
+  auto kdq = bwd_dq_det_kernel<D, ALIBI, DNW, DNST>;
+  constexpr int DQ_LDS = DNST * 2 * 32 * D * 2;
+  static bool dq_attr = false;
+  hipError_t e;
+  if (!dq_attr) {
+    if ((e = set_lds(kdq, DQ_LDS)) != hipSuccess) return e;
+    dq_attr = true;
+  }
+  const int nqb = (p.N + DNW * 32 - 1) / (DNW * 32);
+  hipLaunchKernelGGL(kdq, dim3((unsigned)((int64_t)nqb * p.B * p.H)), dim3(DNW * 64), DQ_LDS, stream, p);
+  return hipGetLastError();
+}
+
+// Pass 3 of the atomic backward: dQ = scale * accumulator, to bf16.
+template <int D>
+static hipError_t launch_convert_d(const BwdParams& p, hipStream_t stream) {
+  const int64_t rows = (int64_t)p.B * p.N * p.H;
+  constexpr int RPB = 256 / (D / 8);
+  hipLaunchKernelGGL(bwd_dq_convert_kernel<D>, dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_prep(const BwdParams& p, int d, bool zero_acc, hipStream_t stream) {
+  return d == 128 ? launch_prep_d<128>(p, zero_acc, stream) : launch_prep_d<64>(p, zero_acc, stream);
+}
+
+hipError_t launch_bwd_dkdv(const BwdParams& p, int d, hipStream_t stream) {
+  const bool alibi = p.alibi != nullptr;
+  if (d == 128) return alibi ? launch_main_d<128, true, true>(p, stream) : launch_main_d<128, false, true>(p, stream);
+  return alibi ? launch_main_d<64, true, true>(p, stream) : launch_main_d<64, false, true>(p, stream);
+}
+
+hipError_t launch_bwd_dq(const BwdParams& p, int d, hipStream_t stream) {
+  const bool alibi = p.alibi != nullptr;
+  if (d == 128) return alibi ? launch_dq_d<128, true>(p, stream) : launch_dq_d<128, false>(p, stream);
+  return alibi ? launch_dq_d<64, true>(p, stream) : launch_dq_d<64, false>(p, stream);
+}
+
+hipError_t launch_bwd_bf16(const BwdParams& p, int d, bool split_dq, hipStream_t stream) {
+  hipError_t e;
+  if (split_dq) {
+    if ((e = launch_bwd_prep(p, d, false, stream)) != hipSuccess) return e;
+    if ((e = launch_bwd_dkdv(p, d, stream)) != hipSuccess) return e;
+    return launch_bwd_dq(p, d, stream);
+  }
+  if ((e = launch_bwd_prep(p, d, true, stream)) != hipSuccess) return e;
   const bool alibi = p.alibi != nullptr;
   if (d == 128) {
-    if (deterministic)
-      return alibi ? launch_bwd_cfg<128, true, true>(p, stream) : launch_bwd_cfg<128, false, true>(p, stream);
-    return alibi ? launch_bwd_cfg<128, true, false>(p, stream) : launch_bwd_cfg<128, false, false>(p, stream);
+    e = alibi ? launch_main_d<128, true, false>(p, stream) : launch_main_d<128, false, false>(p, stream);
+  } else {
+    e = alibi ? launch_main_d<64, true, false>(p, stream) : launch_main_d<64, false, false>(p, stream);
   }
-  if (deterministic)
-    return alibi ? launch_bwd_cfg<64, true, true>(p, stream) : launch_bwd_cfg<64, false, true>(p, stream);
-  return alibi ? launch_bwd_cfg<64, true, false>(p, stream) : launch_bwd_cfg<64, false, false>(p, stream);
+  if (e != hipSuccess) return e;
+  return d == 128 ? launch_convert_d<128>(p, stream) : launch_convert_d<64>(p, stream);
 }
 
 }  // namespace fa2

@@ -83,38 +83,59 @@ fa2_status_t fa2_fwd_f32(const float* q, const float* k, const float* v, float* 
 size_t fa2_bwd_workspace_size(int B, int H, int N, int d) {
   if (B <= 0 || H <= 0 || N <= 0 || (d != 64 && d != 128)) return 0;
   const size_t rows = (size_t)B * H * N;
-  return align256(rows * d * sizeof(float)) + align256(rows * sizeof(float));
+  return align256(rows * sizeof(float)) + align256(rows * d * sizeof(float));
 }
+
+}  // extern "C"
+
+namespace {
+
+// Shared validation of the backward entry points; fills the parameter block.
+// need_* say which pointers the entry point reads or writes.
+fa2_status_t bwd_setup(const void* q, const void* k, const void* v, const void* out, const float* lse,
+                       const void* dout, void* dq, void* dk, void* dv, const void* workspace,
+                       size_t workspace_bytes, size_t workspace_need, int B, int H, int N, int d,
+                       float scale, int causal, int wl, int wr, const float* alibi, bool need_qkv,
+                       bool need_out, bool need_dq, bool need_dkdv, fa2::BwdParams* p, bool* empty) {
+  fa2_status_t st = check_common(B, H, N, d, scale, wl, wr, empty);
+  if (st != FA2_OK || *empty) return st;
+  const void* needed[] = {need_qkv ? q : dout, need_qkv ? k : dout, need_qkv ? v : dout,
+                          need_qkv ? (const void*)lse : dout, need_out ? out : dout, dout,
+                          need_dq ? dq : dout, need_dkdv ? dk : dout, need_dkdv ? dv : dout, workspace};
+  for (const void* ptr : needed)
+    if (!ptr || !aligned16(ptr)) return FA2_ERR_INVALID_ARG;
+  if (alibi && !aligned4(alibi)) return FA2_ERR_INVALID_ARG;
+  if (workspace_bytes < workspace_need) return FA2_ERR_INVALID_ARG;
+  const size_t rows = (size_t)B * H * N;
+  *p = fa2::BwdParams{};
+  p->q = q; p->k = k; p->v = v; p->o = out; p->lse = lse; p->dout = dout;
+  p->dq = dq; p->dk = dk; p->dv = dv;
+  p->delta = reinterpret_cast<float*>(const_cast<void*>(workspace));
+  p->dq_acc = reinterpret_cast<float*>(reinterpret_cast<char*>(const_cast<void*>(workspace)) +
+                                       align256(rows * sizeof(float)));
+  p->alibi = alibi;
+  p->B = B; p->H = H; p->N = N;
+  p->scale = scale;
+  p->scale_log2 = scale * fa2::kLog2e;
+  p->causal = causal ? 1 : 0;
+  p->wl = wl;
+  p->wr = causal ? 0 : wr;
+  return FA2_OK;
+}
+
+size_t delta_bytes(int B, int H, int N) { return align256((size_t)B * H * N * sizeof(float)); }
+
+fa2_status_t hip_status(hipError_t e) { return e == hipSuccess ? FA2_OK : FA2_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
 
 fa2_status_t fa2_bwd(const void* q, const void* k, const void* v, const void* out, const float* lse,
                      const void* dout, void* dq, void* dk, void* dv, void* workspace,
                      size_t workspace_bytes, int B, int H, int N, int d, float softmax_scale,
                      int causal, int window_left, int window_right, const float* alibi_slopes,
                      int deterministic, void* stream) {
-  bool empty = false;
-  fa2_status_t st = check_common(B, H, N, d, softmax_scale, window_left, window_right, &empty);
-  if (st != FA2_OK || empty) return st;
-  if (!q || !k || !v || !out || !lse || !dout || !dq || !dk || !dv || !workspace)
-    return FA2_ERR_INVALID_ARG;
-  const void* ptrs[] = {q, k, v, out, lse, dout, dq, dk, dv, workspace};
-  for (const void* ptr : ptrs)
-    if (!aligned16(ptr)) return FA2_ERR_INVALID_ARG;
-  if (alibi_slopes && !aligned4(alibi_slopes)) return FA2_ERR_INVALID_ARG;
-  if (workspace_bytes < fa2_bwd_workspace_size(B, H, N, d)) return FA2_ERR_INVALID_ARG;
-
-  fa2::BwdParams p{};
-  p.q = q; p.k = k; p.v = v; p.o = out; p.lse = lse; p.dout = dout;
-  p.dq = dq; p.dk = dk; p.dv = dv;
-  const size_t rows = (size_t)B * H * N;
-  p.dq_acc = reinterpret_cast<float*>(workspace);
-  p.delta = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + align256(rows * d * sizeof(float)));
-  p.alibi = alibi_slopes;
-  p.B = B; p.H = H; p.N = N;
-  p.scale = softmax_scale;
-  p.scale_log2 = softmax_scale * fa2::kLog2e;
-  p.causal = causal ? 1 : 0;
-  p.wl = window_left;
-  p.wr = causal ? 0 : window_right;
   // The separate dQ pass (no atomics) is both bitwise repeatable and, on MI355X,
   // faster than accumulating dQ with float atomics, so it serves both values of
   // `deterministic`. FA2_BWD_ATOMIC_DQ=1 selects the atomic variant when
@@ -124,9 +145,51 @@ fa2_status_t fa2_bwd(const void* q, const void* k, const void* v, const void* ou
     const char* env = getenv("FA2_BWD_ATOMIC_DQ");
     if (env && strcmp(env, "1") == 0) split_dq = false;
   }
-  hipError_t e = fa2::launch_bwd_bf16(p, d, split_dq, (hipStream_t)stream);
-  if (e == hipErrorNotSupported) return FA2_ERR_UNSUPPORTED;
-  return e == hipSuccess ? FA2_OK : FA2_ERR_HIP;
+  fa2::BwdParams p;
+  bool empty = false;
+  const size_t need = split_dq ? delta_bytes(B, H, N) : fa2_bwd_workspace_size(B, H, N, d);
+  fa2_status_t st = bwd_setup(q, k, v, out, lse, dout, dq, dk, dv, workspace, workspace_bytes, need, B, H, N, d,
+                              softmax_scale, causal, window_left, window_right, alibi_slopes, true, true, true,
+                              true, &p, &empty);
+  if (st != FA2_OK || empty) return st;
+  return hip_status(fa2::launch_bwd_bf16(p, d, split_dq, (hipStream_t)stream));
+}
+
+fa2_status_t fa2_bwd_prep(const void* out, const void* dout, void* workspace, size_t workspace_bytes, int B, int H,
+                          int N, int d, void* stream) {
+  fa2::BwdParams p;
+  bool empty = false;
+  fa2_status_t st = bwd_setup(nullptr, nullptr, nullptr, out, nullptr, dout, nullptr, nullptr, nullptr, workspace,
+                              workspace_bytes, delta_bytes(B, H, N), B, H, N, d, 1.0f, 0, -1, -1, nullptr, false,
+                              true, false, false, &p, &empty);
+  if (st != FA2_OK || empty) return st;
+  return hip_status(fa2::launch_bwd_prep(p, d, false, (hipStream_t)stream));
+}
+
+fa2_status_t fa2_bwd_dkdv(const void* q, const void* k, const void* v, const float* lse, const void* dout, void* dk,
+                          void* dv, const void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
+                          float softmax_scale, int causal, int window_left, int window_right,
+                          const float* alibi_slopes, void* stream) {
+  fa2::BwdParams p;
+  bool empty = false;
+  fa2_status_t st = bwd_setup(q, k, v, nullptr, lse, dout, nullptr, dk, dv, workspace, workspace_bytes,
+                              delta_bytes(B, H, N), B, H, N, d, softmax_scale, causal, window_left, window_right,
+                              alibi_slopes, true, false, false, true, &p, &empty);
+  if (st != FA2_OK || empty) return st;
+  return hip_status(fa2::launch_bwd_dkdv(p, d, (hipStream_t)stream));
+}
+
+fa2_status_t fa2_bwd_dq(const void* q, const void* k, const void* v, const float* lse, const void* dout, void* dq,
+                        const void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
+                        float softmax_scale, int causal, int window_left, int window_right,
+                        const float* alibi_slopes, void* stream) {
+  fa2::BwdParams p;
+  bool empty = false;
+  fa2_status_t st = bwd_setup(q, k, v, nullptr, lse, dout, dq, nullptr, nullptr, workspace, workspace_bytes,
+                              delta_bytes(B, H, N), B, H, N, d, softmax_scale, causal, window_left, window_right,
+                              alibi_slopes, true, false, true, false, &p, &empty);
+  if (st != FA2_OK || empty) return st;
+  return hip_status(fa2::launch_bwd_dq(p, d, (hipStream_t)stream));
 }
 
 const char* fa2_status_string(fa2_status_t s) {

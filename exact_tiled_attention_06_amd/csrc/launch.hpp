@@ -10,7 +10,12 @@ namespace fa2 {
 
 hipError_t launch_fwd_bf16(const FwdParams& p, int d, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdParams& p, int d, hipStream_t stream);
-// Backward: delta/zeroing pass, the K/V-block pass and the dQ conversion.
-hipError_t launch_bwd_bf16(const BwdParams& p, int d, bool deterministic, hipStream_t stream);
+// Backward. split_dq: D pass, dK/dV pass, dQ pass (no atomics); else D pass with
+// accumulator zeroing, key-block pass with atomic dQ, dQ conversion.
+hipError_t launch_bwd_bf16(const BwdParams& p, int d, bool split_dq, hipStream_t stream);
+// The three passes of the split backward, launched one at a time.
+hipError_t launch_bwd_prep(const BwdParams& p, int d, bool zero_acc, hipStream_t stream);
+hipError_t launch_bwd_dkdv(const BwdParams& p, int d, hipStream_t stream);
+hipError_t launch_bwd_dq(const BwdParams& p, int d, hipStream_t stream);
 
 }  // namespace fa2

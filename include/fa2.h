@@ -77,9 +77,12 @@ fa2_status_t fa2_fwd_f32(const float* q, const float* k, const float* v, float* 
                          void* stream);
 
 /*
- * Bytes of device workspace fa2_bwd needs for this shape (a float32 dQ
- * accumulator [B, H, N, d] and the per-row D = rowsum(dO * O) [B, H, N], each
- * 256-byte aligned). Returns 0 for an empty or invalid shape.
+ * Bytes of device workspace for the backward at this shape: the per-row
+ * D = rowsum(dO * O), float32 [B, H, N], at offset 0, then a float32 dQ
+ * accumulator [B, H, N, d] used only by the atomic variant (each part rounded
+ * up to 256 bytes). The default fa2_bwd and the three pass entry points below
+ * only touch the first part, round_up(4 * B * H * N, 256) bytes, and accept a
+ * workspace of that size. Returns 0 for an empty or invalid shape.
  */
 size_t fa2_bwd_workspace_size(int B, int H, int N, int d);
 
@@ -91,10 +94,9 @@ size_t fa2_bwd_workspace_size(int B, int H, int N, int d);
  *   dS = P * (dP - D), dQ = scale * dS K, dK = scale * dS^T Q.
  * q, k, v, out, dout: bf16 [B, N, H, d] (read); lse: float32 [B, H, N] (read,
  * as written by fa2_fwd with the same arguments); dq, dk, dv: bf16 [B, N, H, d]
- * (written). workspace: device memory of at least fa2_bwd_workspace_size()
- * bytes (workspace_bytes says how much was given; too little is
- * FA2_ERR_INVALID_ARG); its contents need not be initialised and are
- * overwritten. deterministic != 0 guarantees bitwise-repeatable results: dQ is
+ * (written). workspace: device memory (see fa2_bwd_workspace_size;
+ * workspace_bytes says how much was given; too little is FA2_ERR_INVALID_ARG);
+ * its contents need not be initialised and are overwritten. deterministic != 0 guarantees bitwise-repeatable results: dQ is
  * formed by a separate pass over query blocks, without atomics. With
  * deterministic = 0 the library may choose; it currently uses the same pass
  * (the faster one on MI355X). Setting the environment variable
@@ -108,6 +110,34 @@ fa2_status_t fa2_bwd(const void* q, const void* k, const void* v, const void* ou
                      int B, int H, int N, int d, float softmax_scale, int causal,
                      int window_left, int window_right, const float* alibi_slopes,
                      int deterministic, void* stream);
+
+/*
+ * The three passes of fa2_bwd's default (atomic-free) algorithm as separate
+ * calls, for callers that schedule them themselves (for instance the dK/dV
+ * and dQ passes on two streams: both depend only on fa2_bwd_prep). Arguments
+ * mean what they mean for fa2_bwd; the same workspace (at least
+ * round_up(4 * B * H * N, 256) bytes) must be passed to all three, and
+ * fa2_bwd_prep must have completed before the other two read it.
+ *   fa2_bwd_prep: D = rowsum(dO * O) into the workspace.
+ *   fa2_bwd_dkdv: dK and dV, one pass over query blocks per key block
+ *                 (recomputes P and dS; reads D).
+ *   fa2_bwd_dq:   dQ, one pass over key tiles per query block (recomputes P and
+ *                 dS; reads D); no atomics, bitwise repeatable.
+ * Source: the backward-by-recomputation of "AI基础 | Flash Attention"
+ * (section 反向传播), split by output.
+ */
+fa2_status_t fa2_bwd_prep(const void* out, const void* dout, void* workspace, size_t workspace_bytes,
+                          int B, int H, int N, int d, void* stream);
+fa2_status_t fa2_bwd_dkdv(const void* q, const void* k, const void* v, const float* lse,
+                          const void* dout, void* dk, void* dv, const void* workspace,
+                          size_t workspace_bytes, int B, int H, int N, int d, float softmax_scale,
+                          int causal, int window_left, int window_right,
+                          const float* alibi_slopes, void* stream);
+fa2_status_t fa2_bwd_dq(const void* q, const void* k, const void* v, const float* lse,
+                        const void* dout, void* dq, const void* workspace, size_t workspace_bytes,
+                        int B, int H, int N, int d, float softmax_scale, int causal,
+                        int window_left, int window_right, const float* alibi_slopes,
+                        void* stream);
 
 /* Static, human-readable name of a status code. */
 const char* fa2_status_string(fa2_status_t status);

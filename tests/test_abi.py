@@ -31,7 +31,8 @@ def lib():
 
 def test_header_declares_the_documented_entry_points():
     assert header_functions() == sorted(
-        ["fa2_fwd", "fa2_fwd_f32", "fa2_bwd", "fa2_bwd_workspace_size", "fa2_status_string", "fa2_version"])
+        ["fa2_fwd", "fa2_fwd_f32", "fa2_bwd", "fa2_bwd_workspace_size", "fa2_bwd_prep", "fa2_bwd_dkdv",
+         "fa2_bwd_dq", "fa2_status_string", "fa2_version"])
 
 
 def test_library_exports_every_header_symbol(lib):
@@ -116,6 +117,7 @@ BAD_BWD = [
     (dict(ws=None), fa2.FA2_ERR_INVALID_ARG),
     (dict(dk=MISALIGNED), fa2.FA2_ERR_INVALID_ARG),
     (dict(ws_bytes=100), fa2.FA2_ERR_INVALID_ARG),
+    (dict(ws=MISALIGNED), fa2.FA2_ERR_INVALID_ARG),
     (dict(alibi=FAKE + 1), fa2.FA2_ERR_INVALID_ARG),
 ]
 
@@ -129,8 +131,25 @@ def test_backward_empty_problem_is_ok(lib):
     assert lib.fa2_bwd(*bwd_args(B=0, ws=None, ws_bytes=0)) == fa2.FA2_OK
 
 
+def test_pass_entry_points_reject_bad_arguments(lib):
+    ws = 256
+    # prep: null dout, bad d, too-small workspace
+    assert lib.fa2_bwd_prep(FAKE, None, FAKE, ws, 1, 2, 16, 64, None) == fa2.FA2_ERR_INVALID_ARG
+    assert lib.fa2_bwd_prep(FAKE, FAKE, FAKE, ws, 1, 2, 16, 96, None) == fa2.FA2_ERR_UNSUPPORTED
+    assert lib.fa2_bwd_prep(FAKE, FAKE, FAKE, 8, 1, 2, 16, 64, None) == fa2.FA2_ERR_INVALID_ARG
+    assert lib.fa2_bwd_prep(FAKE, FAKE, FAKE, ws, 0, 2, 16, 64, None) == fa2.FA2_OK
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws, 1, 2, 16, 64, 0.125, 1, -1, -1, None, None]
+    assert lib.fa2_bwd_dkdv(*args[:5], None, *args[6:]) == fa2.FA2_ERR_INVALID_ARG          # dk null
+    assert lib.fa2_bwd_dkdv(*args[:13], 0.0, *args[14:]) == fa2.FA2_ERR_INVALID_ARG         # scale
+    assert lib.fa2_bwd_dkdv(*args[:8], 4, *args[9:]) == fa2.FA2_ERR_INVALID_ARG            # workspace
+    dq_args = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws, 1, 2, 16, 64, 0.125, 1, -1, -1, None, None]
+    assert lib.fa2_bwd_dq(*dq_args[:5], None, *dq_args[6:]) == fa2.FA2_ERR_INVALID_ARG      # dq null
+    assert lib.fa2_bwd_dq(*dq_args[:14], -3, *dq_args[15:]) == fa2.FA2_ERR_INVALID_ARG     # window
+    assert lib.fa2_bwd_dq(*dq_args[:11], 128 + 1, *dq_args[12:]) == fa2.FA2_ERR_UNSUPPORTED
+
+
 def test_workspace_size(lib):
-    # float32 dQ accumulator [B,H,N,d] + delta [B,H,N], each rounded up to 256 bytes
+    # delta [B,H,N] + float32 dQ accumulator [B,H,N,d], each rounded up to 256 bytes
     B, H, N, d = 4, 16, 4096, 128
     rows = B * H * N
     up = lambda x: (x + 255) // 256 * 256

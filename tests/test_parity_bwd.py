@@ -120,3 +120,30 @@ def test_full_size_workload_sampled_rows(gpu_lib, number, deterministic):
     assert max(e_q, e_k, e_v) <= TOL_GRAD_REL
     for x in (dq_np, dk_np, dv_np):
         assert np.isfinite(x).all()
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_pass_entry_points_match_fa2_bwd_on_two_streams(gpu_lib, d):
+    """fa2_bwd_prep, then fa2_bwd_dkdv and fa2_bwd_dq on two streams, equal fa2_bwd bitwise."""
+    B, H, N = 2, 3, 450
+    cpu, dev, slopes = gpu_inputs(B, H, N, d, "bf16", seed=44, with_dout=True, alibi=True)
+    sl = slopes.cuda()
+    scale = scale_of(d)
+    out, lse = gpu_lib.flash_attn_fwd(dev["q"], dev["k"], dev["v"], scale, True, (200, 0), sl)
+    ref = gpu_lib.flash_attn_bwd(dev["dout"], dev["q"], dev["k"], dev["v"], out, lse, scale, True, (200, 0), sl)
+    ws_bytes = (B * H * N * 4 + 255) // 256 * 256  # only D is needed by the passes
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    dq, dk, dv = (torch.empty_like(dev["q"]) for _ in range(3))
+    s0 = torch.cuda.current_stream()
+    s1 = torch.cuda.Stream()
+    gpu_lib.fa2_bwd_prep(out, dev["dout"], ws, ws_bytes, B, H, N, d, s0.cuda_stream)
+    ev = torch.cuda.Event()
+    ev.record(s0)
+    s1.wait_event(ev)
+    gpu_lib.fa2_bwd_dkdv(dev["q"], dev["k"], dev["v"], lse, dev["dout"], dk, dv, ws, ws_bytes, B, H, N, d, scale,
+                         1, 200, 0, sl, s0.cuda_stream)
+    gpu_lib.fa2_bwd_dq(dev["q"], dev["k"], dev["v"], lse, dev["dout"], dq, ws, ws_bytes, B, H, N, d, scale, 1,
+                       200, 0, sl, s1.cuda_stream)
+    torch.cuda.synchronize()
+    for x, y in zip((dq, dk, dv), ref):
+        assert torch.equal(x, y)

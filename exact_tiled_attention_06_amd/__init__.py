@@ -7,12 +7,15 @@ raises FA2Error; there is no fallback path.
 
 Low-level functions carry the C names and arguments (fa2_fwd, fa2_fwd_f32,
 fa2_bwd, fa2_bwd_workspace_size, fa2_bwd_prep, fa2_bwd_dkdv, fa2_bwd_dq,
-fa2_status_string, fa2_version); tensors or
+fa2_fwd_varlen, fa2_bwd_varlen, fa2_status_string, fa2_version); tensors or
 raw device addresses (int) are accepted for pointers. The convenience
 functions ``flash_attn_fwd`` / ``flash_attn_bwd`` mirror the parameter list of
 the FlashAttention v2 API on the wmrh.cn article (section 5.1) minus dropout:
 softmax_scale=None (-> 1/sqrt(d)), causal, window_size=(-1, -1), alibi_slopes,
-and deterministic for the backward.
+and deterministic for the backward. ``flash_attn_varlen_fwd`` /
+``flash_attn_varlen_bwd`` take sequences packed as [T, H, d] with int32
+boundaries ``cu_seqlens`` [B + 1] (variable-length batches, section 6 of the
+same article).
 """
 from __future__ import annotations
 
@@ -22,8 +25,9 @@ import os
 
 __all__ = [
     "FA2Error", "LIB_PATH", "load_library", "fa2_fwd", "fa2_fwd_f32", "fa2_bwd",
-    "fa2_bwd_workspace_size", "fa2_bwd_prep", "fa2_bwd_dkdv", "fa2_bwd_dq", "fa2_status_string", "fa2_version", "flash_attn_fwd",
-    "flash_attn_bwd", "FA2_OK", "FA2_ERR_INVALID_ARG", "FA2_ERR_UNSUPPORTED", "FA2_ERR_HIP",
+    "fa2_bwd_workspace_size", "fa2_bwd_prep", "fa2_bwd_dkdv", "fa2_bwd_dq", "fa2_fwd_varlen", "fa2_bwd_varlen",
+    "fa2_status_string", "fa2_version", "flash_attn_fwd", "flash_attn_bwd", "flash_attn_varlen_fwd",
+    "flash_attn_varlen_bwd", "FA2_OK", "FA2_ERR_INVALID_ARG", "FA2_ERR_UNSUPPORTED", "FA2_ERR_HIP",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa2.so")
@@ -49,6 +53,9 @@ SIGNATURES = {
     "fa2_bwd_prep": ([_P, _P, _P, ctypes.c_size_t, _I, _I, _I, _I, _P], _I),
     "fa2_bwd_dkdv": ([_P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _I, _I, _I, _I, _F, _I, _I, _I, _P, _P], _I),
     "fa2_bwd_dq": ([_P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _I, _I, _I, _I, _F, _I, _I, _I, _P, _P], _I),
+    "fa2_fwd_varlen": ([_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _I, _I, _P, _P], _I),
+    "fa2_bwd_varlen": ([_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _I, _I, _I, _I, _F, _I, _I, _I,
+                        _P, _P], _I),
     "fa2_status_string": ([_I], ctypes.c_char_p),
     "fa2_version": ([], _I),
 }
@@ -163,6 +170,23 @@ def fa2_bwd_dq(q, k, v, lse, dout, dq, workspace, workspace_bytes, B, H, N, d, s
     _check(st, "fa2_bwd_dq")
 
 
+def fa2_fwd_varlen(q, k, v, out, lse, cu_seqlens, B, total_tokens, H, d, softmax_scale, causal, window_left,
+                   window_right, alibi_slopes=None, stream=None):
+    st = load_library().fa2_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(cu_seqlens), int(B),
+                                       int(total_tokens), int(H), int(d), float(softmax_scale), int(causal),
+                                       int(window_left), int(window_right), _ptr(alibi_slopes), _stream(stream))
+    _check(st, "fa2_fwd_varlen")
+
+
+def fa2_bwd_varlen(q, k, v, out, lse, dout, dq, dk, dv, cu_seqlens, workspace, workspace_bytes, B, total_tokens, H,
+                   d, softmax_scale, causal, window_left, window_right, alibi_slopes=None, stream=None):
+    st = load_library().fa2_bwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dout), _ptr(dq),
+                                       _ptr(dk), _ptr(dv), _ptr(cu_seqlens), _ptr(workspace), int(workspace_bytes),
+                                       int(B), int(total_tokens), int(H), int(d), float(softmax_scale), int(causal),
+                                       int(window_left), int(window_right), _ptr(alibi_slopes), _stream(stream))
+    _check(st, "fa2_bwd_varlen")
+
+
 # ------------------------------------------------------------------ convenience wrappers
 
 def _check_tensors(*ts):
@@ -226,4 +250,50 @@ def flash_attn_bwd(dout, q, k, v, out, lse, softmax_scale=None, causal=False, wi
     sl = _slopes(alibi_slopes, H, q.device)
     fa2_bwd(q, k, v, out, lse, dout, dq, dk, dv, workspace, workspace.numel() * workspace.element_size(),
             B, H, N, d, scale, int(bool(causal)), window_size[0], window_size[1], sl, int(bool(deterministic)))
+    return dq, dk, dv
+
+
+def _cu(cu_seqlens, device):
+    import torch
+    if not isinstance(cu_seqlens, torch.Tensor) or cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1:
+        raise FA2Error("cu_seqlens must be a 1-D int32 tensor [B + 1]")
+    if cu_seqlens.device != device or not cu_seqlens.is_contiguous():
+        raise FA2Error("cu_seqlens must be contiguous and on the tensors' GPU")
+    return cu_seqlens
+
+
+def flash_attn_varlen_fwd(q, k, v, cu_seqlens, softmax_scale=None, causal=False, window_size=(-1, -1),
+                          alibi_slopes=None):
+    """Packed variable-length forward. q, k, v: bf16 [T, H, d]; cu_seqlens: int32 [B + 1] on the GPU.
+    Returns (out [T, H, d], lse [H, T] float32)."""
+    import torch
+    _check_tensors(q, k, v)
+    if q.dtype != torch.bfloat16:
+        raise FA2Error("packed batches take bf16 tensors")
+    T, H, d = q.shape
+    cu = _cu(cu_seqlens, q.device)
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    out = torch.empty_like(q)
+    lse = torch.empty((H, T), dtype=torch.float32, device=q.device)
+    fa2_fwd_varlen(q, k, v, out, lse, cu, cu.numel() - 1, T, H, d, scale, int(bool(causal)), window_size[0],
+                   window_size[1], _slopes(alibi_slopes, H, q.device))
+    return out, lse
+
+
+def flash_attn_varlen_bwd(dout, q, k, v, out, lse, cu_seqlens, softmax_scale=None, causal=False,
+                          window_size=(-1, -1), alibi_slopes=None, workspace=None):
+    """Packed variable-length backward from the forward's out and lse. Returns (dq, dk, dv) [T, H, d]."""
+    import torch
+    _check_tensors(q, k, v, out, dout)
+    if q.dtype != torch.bfloat16:
+        raise FA2Error("packed batches take bf16 tensors")
+    T, H, d = q.shape
+    cu = _cu(cu_seqlens, q.device)
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    if workspace is None:
+        workspace = torch.empty(max(fa2_bwd_workspace_size(1, H, T, d), 256), dtype=torch.uint8, device=q.device)
+    fa2_bwd_varlen(q, k, v, out, lse, dout, dq, dk, dv, cu, workspace, workspace.numel() * workspace.element_size(),
+                   cu.numel() - 1, T, H, d, scale, int(bool(causal)), window_size[0], window_size[1],
+                   _slopes(alibi_slopes, H, q.device))
     return dq, dk, dv

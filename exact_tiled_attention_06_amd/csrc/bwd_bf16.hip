@@ -26,6 +26,9 @@
 // Deterministic variant: pass 2 skips dQ, and bwd_dq_det_kernel forms dQ per
 // 128-query block by a key sweep shaped like the forward (S^T = K Q^T,
 // dP^T = V dO^T, dQ^T += K^T dS^T), with no atomics.
+// VARLEN (packed sequences of different lengths, deterministic variant only):
+// as in the forward, workgroups cover an upper bound of the blocks present and
+// find their sequence with varlen_block; D and LSE are [H, total tokens].
 #include <type_traits>
 
 #include "common.hpp"
@@ -115,8 +118,33 @@ __global__ __launch_bounds__(256) void bwd_dq_convert_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------- pass 2
-template <int D, bool ALIBI, bool DET, int NW, int NST>
+// Sequence of this workgroup: head h, first token tok0, length N, and stat0, the
+// index of its row 0 in LSE and D. Returns false for a spare workgroup of a
+// packed batch. `rows` is the block size of the calling kernel.
+template <bool VARLEN>
+__device__ __forceinline__ bool bwd_sequence(const BwdParams& p, int rows, bool descending, int& h, int& blk,
+                                             int& N, int64_t& tok0, int64_t& stat0) {
+  int bh;
+  grid_map<kHeadGroup>((int)blockIdx.x, p.nblk, p.B * p.H, descending, bh, blk);
+  if constexpr (VARLEN) {
+    int t0, len;
+    if (!varlen_block(p.cu_seqlens, p.nseq, p.N, rows, blk, blk, t0, len)) return false;
+    h = bh;
+    N = len;
+    tok0 = t0;
+    stat0 = (int64_t)h * p.N + t0;
+  } else {
+    h = bh % p.H;
+    N = p.N;
+    tok0 = (int64_t)(bh / p.H) * N;
+    stat0 = (int64_t)bh * N;
+  }
+  return true;
+}
+
+template <int D, bool ALIBI, bool DET, int NW, int NST, bool VARLEN>
 __global__ __launch_bounds__(NW * 64, ((D == 128 && !DET) ? 4 : 8) / NW) void bwd_main_kernel(BwdParams p) {
+  static_assert(DET || !VARLEN, "packed batches use the split dQ pass");
   using S = BwdShape<D, NW, NST, DET>;
   constexpr int ROWB = 2 * D;
   extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -124,21 +152,20 @@ __global__ __launch_bounds__(NW * 64, ((D == 128 && !DET) ? 4 : 8) / NW) void bw
   char* stage_lds = smem + S::K_BYTES;
   char* ds_lds = stage_lds + 2 * S::STAGE_BYTES;
 
-  int bh, kb;
-  grid_map<kHeadGroup>((int)blockIdx.x, (p.N + S::BK - 1) / S::BK, p.B * p.H, false, bh, kb);  // early keys first
-  const int b = bh / p.H, h = bh % p.H;
-  const int N = p.N;
+  int h, kb, N;
+  int64_t tok0, stat0;
+  if (!bwd_sequence<VARLEN>(p, S::BK, false, h, kb, N, tok0, stat0)) return;  // early keys first
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
   const int g = lane >> 4, j = lane & 15;
   const int64_t rs = (int64_t)p.H * D;
-  const int64_t base = (int64_t)b * N * rs + (int64_t)h * D;
+  const int64_t base = tok0 * rs + (int64_t)h * D;
   const bf16* qg = (const bf16*)p.q + base;
   const bf16* kg = (const bf16*)p.k + base;
   const bf16* vg = (const bf16*)p.v + base;
   const bf16* dog = (const bf16*)p.dout + base;
-  const float* lse_g = p.lse + (int64_t)bh * N;
-  const float* del_g = p.delta + (int64_t)bh * N;
+  const float* lse_g = p.lse + stat0;
+  const float* del_g = p.delta + stat0;
 
   const int k0 = kb * S::BK;
   const int k_last = min(k0 + S::BK, N) - 1;
@@ -347,7 +374,7 @@ __global__ __launch_bounds__(NW * 64, ((D == 128 && !DET) ? 4 : 8) / NW) void bw
         dqa = mfma32(__builtin_shufflevector(a_lo, a_hi, 0, 1, 2, 3, 4, 5, 6, 7),
                      __builtin_shufflevector(b_lo, b_hi, 0, 1, 2, 3, 4, 5, 6, 7), dqa);
       }
-      float* dq_row = p.dq_acc + ((int64_t)bh * N + i0) * D + 32 * mbq + l32;
+      float* dq_row = p.dq_acc + (stat0 + i0) * D + 32 * mbq + l32;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int m = 8 * (r >> 2) + 4 * hh + (r & 3);
@@ -396,7 +423,7 @@ __global__ __launch_bounds__(NW * 64, ((D == 128 && !DET) ? 4 : 8) / NW) void bw
 // dP^T = V dO^T put one query per lane (column), so LSE and D are per-lane
 // scalars, and dS^T feeds dQ^T += K^T dS^T as the B operand straight from
 // registers (K^T read transposed from the K tile).
-template <int D, bool ALIBI, int NW, int NST>
+template <int D, bool ALIBI, int NW, int NST, bool VARLEN>
 __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq_det_kernel(BwdParams p) {
   constexpr int BR = NW * 32, BC = 32;
   constexpr int KS = D / 16, MB = D / 32;
@@ -407,16 +434,15 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq_det_kernel(BwdParams p
   static_assert(TILE % (1024 * NW) == 0, "tile must split into 1 KB pieces per wave");
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
-  int bh, qb;
-  grid_map<kHeadGroup>((int)blockIdx.x, (p.N + BR - 1) / BR, p.B * p.H, true, bh, qb);
-  const int b = bh / p.H, h = bh % p.H;
-  const int N = p.N;
+  int h, qb, N;
+  int64_t tok0, stat0;
+  if (!bwd_sequence<VARLEN>(p, BR, true, h, qb, N, tok0, stat0)) return;  // longest blocks first
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
   const int g = lane >> 4, j = lane & 15;
   const int64_t rs = (int64_t)p.H * D;
-  const int64_t base = (int64_t)b * N * rs + (int64_t)h * D;
+  const int64_t base = tok0 * rs + (int64_t)h * D;
   const bf16* qg = (const bf16*)p.q + base;
   const bf16* kg = (const bf16*)p.k + base;
   const bf16* vg = (const bf16*)p.v + base;
@@ -435,8 +461,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq_det_kernel(BwdParams p
     qf[ks] = qi < N ? *reinterpret_cast<const bf16x8*>(qg + (int64_t)qi * rs + 16 * ks + 8 * hh) : bf16x8{};
     of[ks] = qi < N ? *reinterpret_cast<const bf16x8*>(dog + (int64_t)qi * rs + 16 * ks + 8 * hh) : bf16x8{};
   }
-  const float lse2 = qi < N ? p.lse[(int64_t)bh * N + qi] * kLog2e : INFINITY;
-  const float delta = qi < N ? p.delta[(int64_t)bh * N + qi] : 0.f;
+  const float lse2 = qi < N ? p.lse[stat0 + qi] * kLog2e : INFINITY;
+  const float delta = qi < N ? p.delta[stat0 + qi] : 0.f;
   const float slope2 = ALIBI ? p.alibi[h] * kLog2e : 0.f;
 
   int kv_lo = 0, kv_hi = N;
@@ -599,31 +625,32 @@ static hipError_t launch_prep_d(const BwdParams& p, bool zero_acc, hipStream_t s
 }
 
 // Pass 2: the key-block pass (dK, dV; with DET = false also the atomic dQ).
-template <int D, bool ALIBI, bool DET>
-static hipError_t launch_main_d(const BwdParams& p, hipStream_t stream) {
+template <int D, bool ALIBI, bool DET, bool VARLEN>
+static hipError_t launch_main_d(const BwdParams& p0, hipStream_t stream) {
   // Split dQ pass (DET): deeper Q/dO ring and 8 waves per key block; atomic dQ:
   // 4 waves, 2 stages (its dS^T buffer and dQ step need the room).
   constexpr int NW = DET ? (D == 128 ? FA2_BWD_NW : 4) : 4;
   constexpr int NST = DET ? (D == 128 ? FA2_BWD_NST : 3) : 2;
   using S = BwdShape<D, NW, NST, DET>;
-  auto kmain = bwd_main_kernel<D, ALIBI, DET, NW, NST>;
+  auto kmain = bwd_main_kernel<D, ALIBI, DET, NW, NST, VARLEN>;
   static bool main_attr = false;
   hipError_t e;
   if (!main_attr) {
     if ((e = set_lds(kmain, S::LDS)) != hipSuccess) return e;
     main_attr = true;
   }
-  const int nkb = (p.N + S::BK - 1) / S::BK;
-  hipLaunchKernelGGL(kmain, dim3((unsigned)((int64_t)nkb * p.B * p.H)), dim3(S::NT), S::LDS, stream, p);
+  BwdParams p = p0;
+  p.nblk = VARLEN ? (int)varlen_block_bound(p.N, p.nseq, S::BK) : (p.N + S::BK - 1) / S::BK;
+  hipLaunchKernelGGL(kmain, dim3((unsigned)((int64_t)p.nblk * p.B * p.H)), dim3(S::NT), S::LDS, stream, p);
   return hipGetLastError();
 }
 
 // Pass 3 of the split backward: dQ by a sweep over key tiles per query block.
-template <int D, bool ALIBI>
-static hipError_t launch_dq_d(const BwdParams& p, hipStream_t stream) {
+template <int D, bool ALIBI, bool VARLEN>
+static hipError_t launch_dq_d(const BwdParams& p0, hipStream_t stream) {
   constexpr int DNW = D == 128 ? FA2_DQ_NW : 4;
   constexpr int DNST = FA2_DQ_NST;
-  auto kdq = bwd_dq_det_kernel<D, ALIBI, DNW, DNST>;
+  auto kdq = bwd_dq_det_kernel<D, ALIBI, DNW, DNST, VARLEN>;
   constexpr int DQ_LDS = DNST * 2 * 32 * D * 2;
   static bool dq_attr = false;
   hipError_t e;
@@ -631,8 +658,9 @@ static hipError_t launch_dq_d(const BwdParams& p, hipStream_t stream) {
     if ((e = set_lds(kdq, DQ_LDS)) != hipSuccess) return e;
     dq_attr = true;
   }
-  const int nqb = (p.N + DNW * 32 - 1) / (DNW * 32);
-  hipLaunchKernelGGL(kdq, dim3((unsigned)((int64_t)nqb * p.B * p.H)), dim3(DNW * 64), DQ_LDS, stream, p);
+  BwdParams p = p0;
+  p.nblk = VARLEN ? (int)varlen_block_bound(p.N, p.nseq, DNW * 32) : (p.N + DNW * 32 - 1) / (DNW * 32);
+  hipLaunchKernelGGL(kdq, dim3((unsigned)((int64_t)p.nblk * p.B * p.H)), dim3(DNW * 64), DQ_LDS, stream, p);
   return hipGetLastError();
 }
 
@@ -649,16 +677,27 @@ hipError_t launch_bwd_prep(const BwdParams& p, int d, bool zero_acc, hipStream_t
   return d == 128 ? launch_prep_d<128>(p, zero_acc, stream) : launch_prep_d<64>(p, zero_acc, stream);
 }
 
+template <int D, bool VARLEN>
+static hipError_t launch_dkdv_v(const BwdParams& p, hipStream_t stream) {
+  return p.alibi != nullptr ? launch_main_d<D, true, true, VARLEN>(p, stream)
+                            : launch_main_d<D, false, true, VARLEN>(p, stream);
+}
+
+template <int D, bool VARLEN>
+static hipError_t launch_dq_v(const BwdParams& p, hipStream_t stream) {
+  return p.alibi != nullptr ? launch_dq_d<D, true, VARLEN>(p, stream) : launch_dq_d<D, false, VARLEN>(p, stream);
+}
+
 hipError_t launch_bwd_dkdv(const BwdParams& p, int d, hipStream_t stream) {
-  const bool alibi = p.alibi != nullptr;
-  if (d == 128) return alibi ? launch_main_d<128, true, true>(p, stream) : launch_main_d<128, false, true>(p, stream);
-  return alibi ? launch_main_d<64, true, true>(p, stream) : launch_main_d<64, false, true>(p, stream);
+  const bool varlen = p.cu_seqlens != nullptr;
+  if (d == 128) return varlen ? launch_dkdv_v<128, true>(p, stream) : launch_dkdv_v<128, false>(p, stream);
+  return varlen ? launch_dkdv_v<64, true>(p, stream) : launch_dkdv_v<64, false>(p, stream);
 }
 
 hipError_t launch_bwd_dq(const BwdParams& p, int d, hipStream_t stream) {
-  const bool alibi = p.alibi != nullptr;
-  if (d == 128) return alibi ? launch_dq_d<128, true>(p, stream) : launch_dq_d<128, false>(p, stream);
-  return alibi ? launch_dq_d<64, true>(p, stream) : launch_dq_d<64, false>(p, stream);
+  const bool varlen = p.cu_seqlens != nullptr;
+  if (d == 128) return varlen ? launch_dq_v<128, true>(p, stream) : launch_dq_v<128, false>(p, stream);
+  return varlen ? launch_dq_v<64, true>(p, stream) : launch_dq_v<64, false>(p, stream);
 }
 
 hipError_t launch_bwd_bf16(const BwdParams& p, int d, bool split_dq, hipStream_t stream) {
@@ -668,12 +707,13 @@ hipError_t launch_bwd_bf16(const BwdParams& p, int d, bool split_dq, hipStream_t
     if ((e = launch_bwd_dkdv(p, d, stream)) != hipSuccess) return e;
     return launch_bwd_dq(p, d, stream);
   }
+  if (p.cu_seqlens != nullptr) return hipErrorInvalidValue;  // packed batches: split dQ only
   if ((e = launch_bwd_prep(p, d, true, stream)) != hipSuccess) return e;
   const bool alibi = p.alibi != nullptr;
   if (d == 128) {
-    e = alibi ? launch_main_d<128, true, false>(p, stream) : launch_main_d<128, false, false>(p, stream);
+    e = alibi ? launch_main_d<128, true, false, false>(p, stream) : launch_main_d<128, false, false, false>(p, stream);
   } else {
-    e = alibi ? launch_main_d<64, true, false>(p, stream) : launch_main_d<64, false, false>(p, stream);
+    e = alibi ? launch_main_d<64, true, false, false>(p, stream) : launch_main_d<64, false, false, false>(p, stream);
   }
   if (e != hipSuccess) return e;
   return d == 128 ? launch_convert_d<128>(p, stream) : launch_convert_d<64>(p, stream);

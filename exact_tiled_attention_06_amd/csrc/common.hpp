@@ -198,6 +198,53 @@ __device__ __forceinline__ void grid_map(int id, int nblk, int bh_count, bool de
   blk = descending ? nblk - 1 - r : r;
 }
 
+// Variable-length batches: nseq sequences packed along the token axis, sequence
+// s holding tokens cu[s] .. cu[s+1]-1 of `total`. Blocks of `rows` tokens are
+// numbered sequence by sequence (sequence s has ceil(len_s / rows) of them).
+// Maps virtual block v to (block index within its sequence, first token,
+// length); returns false when v lies past the last block. The 64 lanes of a
+// wave take 64 sequences at a time: block counts, an inclusive prefix sum
+// across the wave, then a ballot for the first prefix above v. Every wave
+// computes the same, uniform answer. Boundaries are clamped into [0, total]
+// and each end to at least its start, so malformed offsets cannot address
+// memory outside the packed tensors.
+__device__ __forceinline__ bool varlen_block(const int* cu, int nseq, int total, int rows, int v, int& blk,
+                                             int& tok0, int& len) {
+  const int lane = threadIdx.x & 63;
+  int rem = v;
+  for (int c = 0; c < nseq; c += 64) {
+    const int s = c + lane;
+    int a = 0, e = 0;
+    if (s < nseq) {
+      a = min(max(cu[s], 0), total);
+      e = min(max(cu[s + 1], a), total);
+    }
+    const int nb = (e - a + rows - 1) / rows;
+    int incl = nb;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += y;
+    }
+    const uint64_t hit = __builtin_amdgcn_ballot_w64(incl > rem);
+    if (hit != 0) {
+      const int L = __builtin_ctzll(hit);
+      blk = __builtin_amdgcn_readfirstlane(rem - (__shfl(incl, L, 64) - __shfl(nb, L, 64)));
+      tok0 = __builtin_amdgcn_readfirstlane(__shfl(a, L, 64));
+      len = __builtin_amdgcn_readfirstlane(__shfl(e - a, L, 64));
+      return true;
+    }
+    rem -= __builtin_amdgcn_readfirstlane(__shfl(incl, 63, 64));
+  }
+  return false;
+}
+
+// Upper bound on the number of virtual blocks of a packed batch: sum over
+// sequences of ceil(len_s / rows) <= (total + nseq * (rows - 1)) / rows.
+__host__ __device__ inline int64_t varlen_block_bound(int total, int nseq, int rows) {
+  return ((int64_t)total + (int64_t)nseq * (rows - 1)) / rows;
+}
+
 struct FwdParams {
   const void* q;
   const void* k;
@@ -205,8 +252,10 @@ struct FwdParams {
   void* o;
   float* lse;
   const float* alibi;  // [H] or null
-  int B, H, N;
-  int n_qblocks;
+  int B, H, N;       // packed batches: B = 1, N = total tokens
+  int n_qblocks;     // query blocks per head (packed batches: the virtual-block bound)
+  const int* cu_seqlens;  // [nseq + 1] sequence boundaries of a packed batch, or null
+  int nseq;
   float scale;       // softmax scale
   float scale_log2;  // softmax scale * log2(e)
   int causal;
@@ -227,7 +276,10 @@ struct BwdParams {
   float* dq_acc;  // [B, H, N, d] float32 workspace
   float* delta;   // [B, H, N] float32 workspace
   const float* alibi;
-  int B, H, N;
+  int B, H, N;       // packed batches: B = 1, N = total tokens
+  int nblk;          // blocks per head of the kernel being launched (packed: virtual-block bound)
+  const int* cu_seqlens;  // [nseq + 1] sequence boundaries of a packed batch, or null
+  int nseq;
   float scale;
   float scale_log2;
   int causal;

@@ -192,6 +192,67 @@ fa2_status_t fa2_bwd_dq(const void* q, const void* k, const void* v, const float
   return hip_status(fa2::launch_bwd_dq(p, d, (hipStream_t)stream));
 }
 
+}  // extern "C"
+
+namespace {
+
+// Checks shared by the packed (variable-length) entry points. The packed
+// tensors are handed to the fixed-length checks as one batch of `total` tokens.
+fa2_status_t check_varlen(const int* cu_seqlens, int B, int total, int H, int d, float scale, int wl, int wr,
+                          bool* empty) {
+  *empty = false;
+  if (B < 0 || total < 0 || B == INT32_MAX) return FA2_ERR_INVALID_ARG;
+  if (B == 0 && total > 0) return FA2_ERR_INVALID_ARG;  // no sequence can hold the tokens
+  fa2_status_t st = check_common(1, H, total, d, scale, wl, wr, empty);
+  if (st != FA2_OK) return st;
+  // virtual-block bound (largest for 32-row blocks) times H must fit the grid
+  if (fa2::varlen_block_bound(total, B, 32) * H > (int64_t)INT32_MAX) return FA2_ERR_UNSUPPORTED;
+  if (B == 0) *empty = true;
+  if (*empty) return FA2_OK;
+  if (!cu_seqlens || !aligned4(cu_seqlens)) return FA2_ERR_INVALID_ARG;
+  return FA2_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+fa2_status_t fa2_fwd_varlen(const void* q, const void* k, const void* v, void* out, float* lse,
+                            const int* cu_seqlens, int B, int total_tokens, int H, int d, float softmax_scale,
+                            int causal, int window_left, int window_right, const float* alibi_slopes,
+                            void* stream) {
+  bool empty = false;
+  fa2_status_t st = check_varlen(cu_seqlens, B, total_tokens, H, d, softmax_scale, window_left, window_right, &empty);
+  if (st != FA2_OK || empty) return st;
+  if (!q || !k || !v || !out || !lse) return FA2_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(lse))
+    return FA2_ERR_INVALID_ARG;
+  if (alibi_slopes && !aligned4(alibi_slopes)) return FA2_ERR_INVALID_ARG;
+  fa2::FwdParams p = fwd_params(q, k, v, out, lse, 1, H, total_tokens, softmax_scale, causal, window_left,
+                                window_right, alibi_slopes);
+  p.cu_seqlens = cu_seqlens;
+  p.nseq = B;
+  return hip_status(fa2::launch_fwd_bf16(p, d, (hipStream_t)stream));
+}
+
+fa2_status_t fa2_bwd_varlen(const void* q, const void* k, const void* v, const void* out, const float* lse,
+                            const void* dout, void* dq, void* dk, void* dv, const int* cu_seqlens, void* workspace,
+                            size_t workspace_bytes, int B, int total_tokens, int H, int d, float softmax_scale,
+                            int causal, int window_left, int window_right, const float* alibi_slopes,
+                            void* stream) {
+  bool empty = false;
+  fa2_status_t st = check_varlen(cu_seqlens, B, total_tokens, H, d, softmax_scale, window_left, window_right, &empty);
+  if (st != FA2_OK || empty) return st;
+  fa2::BwdParams p;
+  st = bwd_setup(q, k, v, out, lse, dout, dq, dk, dv, workspace, workspace_bytes, delta_bytes(1, H, total_tokens), 1,
+                 H, total_tokens, d, softmax_scale, causal, window_left, window_right, alibi_slopes, true, true, true,
+                 true, &p, &empty);
+  if (st != FA2_OK || empty) return st;
+  p.cu_seqlens = cu_seqlens;
+  p.nseq = B;
+  return hip_status(fa2::launch_bwd_bf16(p, d, true, (hipStream_t)stream));
+}
+
 const char* fa2_status_string(fa2_status_t s) {
   switch (s) {
     case FA2_OK: return "FA2_OK";

@@ -24,13 +24,20 @@
 //    the output is rescaled only when some row's max grew by more than
 //    2^kRescaleLog2 — every P then stays <= 2^kRescaleLog2 — which is exact:
 //    numerator and denominator share the same reference max.
-//  * K/V tiles: register-staged global loads for tile t+1 are issued before
-//    the MFMAs of tile t, written to the other half of a 2-stage LDS ring
-//    afterwards; one barrier per tile. LDS rows are XOR-swizzled in 16-byte
-//    chunks so that the 16-byte K reads and the transposed V reads are free of
-//    bank conflicts.
+//  * K/V tiles go straight from global memory into an NST-stage LDS ring
+//    (global_load_lds_dwordx4); the loads of tile t + NST - 1 are issued before
+//    the MFMAs of tile t, and one barrier per tile hands a stage over. LDS rows
+//    are XOR-swizzled in 16-byte chunks so that the 16-byte K reads and the
+//    transposed V reads are free of bank conflicts.
 //  * Causal / windowed grids run the longest query blocks first; masks are
 //    evaluated only on tiles that cross a mask edge or the end of the sequence.
+//  * VARLEN: sequences of different lengths packed along the token axis (the
+//    variable-length batches of the wmrh.cn FlashAttention v2 article, section
+//    6). The grid covers an upper bound of the query blocks actually present
+//    (not B x the longest sequence); each workgroup finds its sequence from the
+//    boundaries (varlen_block) and the few spare workgroups exit at once.
+//    Everything after that is the fixed-length code with the sequence's start,
+//    length and LSE row.
 #include <type_traits>
 
 #include "common.hpp"
@@ -59,7 +66,7 @@ struct FwdShape {
   static constexpr int ROWB = 2 * D;        // bytes per LDS row
 };
 
-template <int D, int NW, int BC, int NST, bool ALIBI>
+template <int D, int NW, int BC, int NST, bool ALIBI, bool VARLEN>
 __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(FwdParams p) {
   using S = FwdShape<D, NW, BC, NST>;
   constexpr int PER_WAVE = S::PER_WAVE;
@@ -67,15 +74,28 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(FwdParams p) 
 
   int bh, qb;
   grid_map<kHeadGroup>((int)blockIdx.x, p.n_qblocks, p.B * p.H, true, bh, qb);  // longest blocks first
-  const int b = bh / p.H, h = bh % p.H;
-  const int N = p.N;
+  int h, N;
+  int64_t tok0, stat0;  // first token of the sequence; index of its row 0 in lse
+  if constexpr (VARLEN) {
+    int t0, len;
+    if (!varlen_block(p.cu_seqlens, p.nseq, p.N, S::BR, qb, qb, t0, len)) return;
+    h = bh;
+    N = len;
+    tok0 = t0;
+    stat0 = (int64_t)h * p.N + t0;
+  } else {
+    h = bh % p.H;
+    N = p.N;
+    tok0 = (int64_t)(bh / p.H) * N;
+    stat0 = (int64_t)bh * N;
+  }
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
   const int lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
   const int g = lane >> 4, j = lane & 15;
   const int64_t rs = (int64_t)p.H * D;  // elements between consecutive tokens
-  const int64_t base = (int64_t)b * N * rs + (int64_t)h * D;
+  const int64_t base = tok0 * rs + (int64_t)h * D;
   const bf16* qg = (const bf16*)p.q + base;
   const bf16* kg = (const bf16*)p.k + base;
   const bf16* vg = (const bf16*)p.v + base;
@@ -282,16 +302,16 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(FwdParams p) 
         *reinterpret_cast<bf16x4*>(orow + 32 * mb + 8 * a + 4 * hh) = val;
       }
     }
-    if (hh == 0) p.lse[(int64_t)bh * N + qi] = lt > 0.f ? (m2 + log2f(lt)) * kLn2 : -INFINITY;
+    if (hh == 0) p.lse[stat0 + qi] = lt > 0.f ? (m2 + log2f(lt)) * kLn2 : -INFINITY;
   }
 }
 
-template <int D, int NW, int BC, int NST, bool ALIBI>
+template <int D, int NW, int BC, int NST, bool ALIBI, bool VARLEN>
 static hipError_t launch_fwd_cfg(const FwdParams& p0, hipStream_t stream) {
   using S = FwdShape<D, NW, BC, NST>;
   FwdParams p = p0;
-  p.n_qblocks = (p.N + S::BR - 1) / S::BR;
-  auto kern = fwd_bf16_kernel<D, NW, BC, NST, ALIBI>;
+  p.n_qblocks = VARLEN ? (int)varlen_block_bound(p.N, p.nseq, S::BR) : (p.N + S::BR - 1) / S::BR;
+  auto kern = fwd_bf16_kernel<D, NW, BC, NST, ALIBI, VARLEN>;
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, S::LDS);
@@ -310,14 +330,17 @@ static hipError_t launch_fwd_cfg(const FwdParams& p0, hipStream_t stream) {
 #define FA2_FWD_NST 2
 #endif
 
-hipError_t launch_fwd_bf16(const FwdParams& p, int d, hipStream_t stream) {
+template <int D, bool VARLEN>
+static hipError_t launch_fwd_d(const FwdParams& p, hipStream_t stream) {
   constexpr int NW = FA2_FWD_NW, NST = FA2_FWD_NST;
-  const bool alibi = p.alibi != nullptr;
-  if (d == 128) {
-    return alibi ? launch_fwd_cfg<128, NW, 64, NST, true>(p, stream)
-                 : launch_fwd_cfg<128, NW, 64, NST, false>(p, stream);
-  }
-  return alibi ? launch_fwd_cfg<64, NW, 64, NST, true>(p, stream) : launch_fwd_cfg<64, NW, 64, NST, false>(p, stream);
+  return p.alibi != nullptr ? launch_fwd_cfg<D, NW, 64, NST, true, VARLEN>(p, stream)
+                            : launch_fwd_cfg<D, NW, 64, NST, false, VARLEN>(p, stream);
+}
+
+hipError_t launch_fwd_bf16(const FwdParams& p, int d, hipStream_t stream) {
+  const bool varlen = p.cu_seqlens != nullptr;
+  if (d == 128) return varlen ? launch_fwd_d<128, true>(p, stream) : launch_fwd_d<128, false>(p, stream);
+  return varlen ? launch_fwd_d<64, true>(p, stream) : launch_fwd_d<64, false>(p, stream);
 }
 
 }  // namespace fa2

@@ -139,6 +139,49 @@ fa2_status_t fa2_bwd_dq(const void* q, const void* k, const void* v, const float
                         int window_left, int window_right, const float* alibi_slopes,
                         void* stream);
 
+/*
+ * Variable-length batches: B sequences of different lengths packed along the
+ * token axis, with no padding. The wmrh.cn FlashAttention v2 article (section
+ * 6, future directions) names variable-length sequences, handled with
+ * padding-aware scheduling, as the method's open inefficiency; the page gives
+ * no interface, so this one is:
+ *   - q, k, v, out, dout, dq, dk, dv: contiguous [total_tokens, H, d] bf16;
+ *   - cu_seqlens: DEVICE int32 [B + 1], cu_seqlens[0] = 0, non-decreasing,
+ *     cu_seqlens[B] = total_tokens; sequence b holds tokens cu_seqlens[b] ..
+ *     cu_seqlens[b + 1] - 1 and may be empty. The library cannot check the
+ *     contents without a synchronisation: other contents give unspecified
+ *     results, but every access stays inside the packed tensors (offsets are
+ *     clamped into [0, total_tokens]);
+ *   - lse (and the backward's D in the workspace): float32 [H, total_tokens];
+ *   - every sequence is its own attention problem: a query sees only the keys
+ *     of its own sequence, and positions for causal, window_left/right and
+ *     ALiBi count from the sequence's first token. Queries and keys share the
+ *     boundaries (self-attention).
+ * Only the query blocks present are scheduled: the grid covers
+ * (total_tokens + B * (rows - 1)) / rows blocks per head for a kernel of
+ * `rows`-token blocks, and each workgroup finds its sequence on the device.
+ * B = 0 with total_tokens = 0, total_tokens = 0 or H = 0 is an empty problem
+ * (FA2_OK, nothing launched); B = 0 with total_tokens > 0 is
+ * FA2_ERR_INVALID_ARG. Other arguments and errors as for fa2_fwd / fa2_bwd.
+ */
+fa2_status_t fa2_fwd_varlen(const void* q, const void* k, const void* v, void* out, float* lse,
+                            const int* cu_seqlens, int B, int total_tokens, int H, int d,
+                            float softmax_scale, int causal, int window_left, int window_right,
+                            const float* alibi_slopes, void* stream);
+
+/*
+ * Backward of fa2_fwd_varlen (same arguments, plus dout, dq, dk, dv and a
+ * workspace of at least round_up(4 * H * total_tokens, 256) bytes, which
+ * fa2_bwd_workspace_size(1, H, total_tokens, d) covers). Always the
+ * atomic-free algorithm (D pass, dK/dV pass, dQ pass): bitwise repeatable.
+ */
+fa2_status_t fa2_bwd_varlen(const void* q, const void* k, const void* v, const void* out,
+                            const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                            const int* cu_seqlens, void* workspace, size_t workspace_bytes,
+                            int B, int total_tokens, int H, int d, float softmax_scale, int causal,
+                            int window_left, int window_right, const float* alibi_slopes,
+                            void* stream);
+
 /* Static, human-readable name of a status code. */
 const char* fa2_status_string(fa2_status_t status);
 

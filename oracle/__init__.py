@@ -14,3 +14,10 @@ from .attention import (  # noqa: F401
     to_f64,
     visible,
 )
+from .varlen import (  # noqa: F401
+    sequence_bounds,
+    varlen_backward,
+    varlen_backward_sampled,
+    varlen_forward,
+    varlen_forward_rows,
+)

@@ -32,7 +32,7 @@ def lib():
 def test_header_declares_the_documented_entry_points():
     assert header_functions() == sorted(
         ["fa2_fwd", "fa2_fwd_f32", "fa2_bwd", "fa2_bwd_workspace_size", "fa2_bwd_prep", "fa2_bwd_dkdv",
-         "fa2_bwd_dq", "fa2_status_string", "fa2_version"])
+         "fa2_bwd_dq", "fa2_fwd_varlen", "fa2_bwd_varlen", "fa2_status_string", "fa2_version"])
 
 
 def test_library_exports_every_header_symbol(lib):
@@ -146,6 +146,57 @@ def test_pass_entry_points_reject_bad_arguments(lib):
     assert lib.fa2_bwd_dq(*dq_args[:5], None, *dq_args[6:]) == fa2.FA2_ERR_INVALID_ARG      # dq null
     assert lib.fa2_bwd_dq(*dq_args[:14], -3, *dq_args[15:]) == fa2.FA2_ERR_INVALID_ARG     # window
     assert lib.fa2_bwd_dq(*dq_args[:11], 128 + 1, *dq_args[12:]) == fa2.FA2_ERR_UNSUPPORTED
+
+
+def varlen_fwd_args(**over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, lse=FAKE, cu=FAKE, B=3, T=100, H=2, d=64, scale=0.125, causal=1,
+             wl=-1, wr=-1, alibi=None, stream=None)
+    a.update(over)
+    return [a["q"], a["k"], a["v"], a["out"], a["lse"], a["cu"], a["B"], a["T"], a["H"], a["d"], a["scale"],
+            a["causal"], a["wl"], a["wr"], a["alibi"], a["stream"]]
+
+
+def varlen_bwd_args(**over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, lse=FAKE, dout=FAKE, dq=FAKE, dk=FAKE, dv=FAKE, cu=FAKE, ws=FAKE,
+             ws_bytes=1024, B=3, T=100, H=2, d=64, scale=0.125, causal=1, wl=-1, wr=-1, alibi=None, stream=None)
+    a.update(over)
+    return [a[k] for k in ("q", "k", "v", "out", "lse", "dout", "dq", "dk", "dv", "cu", "ws", "ws_bytes", "B", "T",
+                           "H", "d", "scale", "causal", "wl", "wr", "alibi", "stream")]
+
+
+BAD_VARLEN = [
+    (dict(cu=None), fa2.FA2_ERR_INVALID_ARG),
+    (dict(cu=FAKE + 2), fa2.FA2_ERR_INVALID_ARG),
+    (dict(B=-1), fa2.FA2_ERR_INVALID_ARG),
+    (dict(T=-5), fa2.FA2_ERR_INVALID_ARG),
+    (dict(B=0), fa2.FA2_ERR_INVALID_ARG),          # tokens but no sequence
+    (dict(d=96), fa2.FA2_ERR_UNSUPPORTED),
+    (dict(scale=0.0), fa2.FA2_ERR_INVALID_ARG),
+    (dict(wl=-3), fa2.FA2_ERR_INVALID_ARG),
+    (dict(q=None), fa2.FA2_ERR_INVALID_ARG),
+    (dict(lse=MISALIGNED), fa2.FA2_ERR_INVALID_ARG),
+    (dict(alibi=FAKE + 1), fa2.FA2_ERR_INVALID_ARG),
+]
+
+
+@pytest.mark.parametrize("over,status", BAD_VARLEN)
+def test_varlen_entry_points_reject_bad_arguments(lib, over, status):
+    assert lib.fa2_fwd_varlen(*varlen_fwd_args(**over)) == status
+    assert lib.fa2_bwd_varlen(*varlen_bwd_args(**over)) == status
+
+
+def test_varlen_backward_checks_workspace_and_gradients(lib):
+    need = fa2.fa2_bwd_workspace_size(1, 2, 100, 64)
+    assert need >= 2 * 100 * 4
+    assert lib.fa2_bwd_varlen(*varlen_bwd_args(ws_bytes=2 * 100 * 4 - 4)) == fa2.FA2_ERR_INVALID_ARG
+    assert lib.fa2_bwd_varlen(*varlen_bwd_args(dk=None)) == fa2.FA2_ERR_INVALID_ARG
+    assert lib.fa2_bwd_varlen(*varlen_bwd_args(dout=MISALIGNED)) == fa2.FA2_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("over", [dict(T=0), dict(B=0, T=0), dict(H=0), dict(T=0, cu=None, q=None)])
+def test_varlen_empty_problem_is_ok_and_launches_nothing(lib, over):
+    assert lib.fa2_fwd_varlen(*varlen_fwd_args(**over)) == fa2.FA2_OK
+    assert lib.fa2_bwd_varlen(*varlen_bwd_args(**over)) == fa2.FA2_OK
 
 
 def test_workspace_size(lib):

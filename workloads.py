@@ -10,8 +10,15 @@ Recipe (the same for every workload):
     ``Tensor.to(torch.bfloat16)``); both sides then read the same bf16 values;
   * ALiBi slopes, when a workload uses them, are ``2**(-8*(h+1)/H)`` for head
     ``h = 0..H-1``, stored as float32;
-  * the default input seed is the workload number (1..5) and the default
+  * the default input seed is the workload number and the default
     row-sampling seed is ``1000 + number``.
+
+Variable-length batches pack B sequences along the token axis ([T, H, d]
+tensors, T = total tokens) with boundaries ``cu_seqlens`` ([B + 1] int32).
+Their lengths come from B - 1 distinct cut points drawn uniformly from
+1 .. T - 1 with ``numpy.random.default_rng(seed)``: a ragged mix of short and
+long sequences (spacings of uniform cut points, mean T / B). The tensors are
+drawn like a [1, T, H, d] batch and viewed as [T, H, d].
 """
 from __future__ import annotations
 
@@ -111,3 +118,80 @@ def sample_key_rows(B, H, N, count=256, max_heads=4, seed=0):
         for j in js:
             rows.append((bh // H, bh % H, j))
     return np.array(rows, dtype=np.int64)
+
+
+@dataclasses.dataclass(frozen=True)
+class VarlenWorkload:
+    number: int
+    name: str
+    dtype: str
+    total: int          # packed tokens T
+    nseq: int           # sequences B
+    H: int
+    d: int
+    causal: bool
+    window: tuple
+    alibi: bool
+    backward: bool
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+    @property
+    def torch_dtype(self):
+        return torch.float32 if self.dtype == "f32" else torch.bfloat16
+
+    def describe(self) -> str:
+        w = "" if self.window == (-1, -1) else f" window={self.window}"
+        return (f"{self.name}: {self.dtype} T={self.total} B={self.nseq} H={self.H} d={self.d}"
+                f" causal={int(self.causal)}{w} alibi={int(self.alibi)}")
+
+
+# The same token budget and head shape as the causal N=8192 workload (4 x 8192
+# tokens, H=32, d=128), split into 12 ragged sequences.
+VARLEN_WORKLOADS = {
+    6: VarlenWorkload(6, "bf16_varlen_causal_t32768_d128", "bf16", 32768, 12, 32, 128, True, (-1, -1), False, True),
+}
+
+
+def varlen_lengths(total: int, nseq: int, seed: int = 0) -> np.ndarray:
+    """Lengths of nseq sequences (each >= 1) summing to total: spacings of nseq - 1
+    distinct uniform cut points in 1 .. total - 1."""
+    if nseq <= 0:
+        return np.zeros(0, dtype=np.int64)
+    rng = np.random.default_rng(seed)
+    cuts = np.sort(rng.choice(np.arange(1, total), size=nseq - 1, replace=False))
+    edges = np.concatenate([[0], cuts, [total]])
+    return np.diff(edges).astype(np.int64)
+
+
+def cu_seqlens_from_lengths(lengths) -> torch.Tensor:
+    """Sequence boundaries [B + 1] int32: 0, then the running total of the lengths."""
+    lengths = np.asarray(lengths, dtype=np.int64)
+    return torch.from_numpy(np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32))
+
+
+def make_varlen_inputs(total, H, d, dtype="bf16", seed=0, with_dout=False):
+    """Packed q, k, v (and dout) of shape [T, H, d], drawn like a [1, T, H, d] batch."""
+    t = make_inputs(1, H, total, d, dtype, seed, with_dout)
+    return {nm: x[0] for nm, x in t.items()}
+
+
+def varlen_workload_inputs(w: VarlenWorkload, seed=None, with_dout=None):
+    """Inputs of a variable-length workload: tensors, lengths, cu_seqlens and ALiBi slopes."""
+    seed = w.number if seed is None else seed
+    with_dout = w.backward if with_dout is None else with_dout
+    t = make_varlen_inputs(w.total, w.H, w.d, w.dtype, seed, with_dout)
+    t["lengths"] = varlen_lengths(w.total, w.nseq, seed)
+    t["cu_seqlens"] = cu_seqlens_from_lengths(t["lengths"])
+    t["alibi_slopes"] = alibi_slopes(w.H) if w.alibi else None
+    return t
+
+
+def sample_varlen_rows(total, H, count=256, seed=0):
+    """`count` distinct (h, t) pairs (head, packed token) drawn uniformly with the seed, sorted."""
+    rng = np.random.default_rng(seed)
+    count = min(count, total * H)
+    flat = np.sort(rng.choice(total * H, size=count, replace=False))
+    return np.stack([flat // total, flat % total], axis=1).astype(np.int64)

@@ -1,12 +1,18 @@
 """Benchmark: exact attention forward + backward on one MI355X.
 
-A step is one pass of the whole hot path over one batch: fa2_fwd then fa2_bwd
-(delta pass, key-block pass, dQ conversion) on the causal N=8192, d=128 bf16
-workload (B=4, H=32), inputs resident in HBM. FLOPs follow the convention
-of the workload definition: forward 4*B*H*N^2*d, halved for causal; backward
-2.5x forward. Prints ONE JSON line.
+A step is one pass of the whole hot path over one batch: fa2_fwd then the
+backward's three passes (D = rowsum(dO*O), dK/dV pass, dQ pass; exactly what
+fa2_bwd runs) on the causal N=8192, d=128 bf16 workload (B=4, H=32), inputs
+resident in HBM. FLOPs follow the convention of the workload definition:
+forward 4*B*H*N^2*d, halved for causal; backward 2.5x forward. Prints ONE JSON
+line.
 
-  python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+After the timed steps, the packed variable-length workload (32768 tokens in 12
+ragged sequences, H=32, d=128, causal) is timed the same way through
+fa2_fwd_varlen / fa2_bwd_varlen and reported under "varlen", with the FLOP
+convention applied per sequence.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-varlen]
 """
 from __future__ import annotations
 
@@ -64,6 +70,68 @@ def cpu_baseline(w, min_seconds=10.0, max_heads=16):
     }
 
 
+def timed(phases, steps, warmup, stream):
+    """Average milliseconds of each (name, fn) phase over `steps` passes, HIP events on `stream`."""
+    import torch
+    for _ in range(warmup):
+        for _, fn in phases:
+            fn()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(phases) + 1)] for _ in range(steps)]
+    for i in range(steps):
+        ev[i][0].record(stream)
+        for n, (_, fn) in enumerate(phases):
+            fn()
+            ev[i][n + 1].record(stream)
+    torch.cuda.synchronize()
+    return {name: sum(e[n].elapsed_time(e[n + 1]) for e in ev) / steps for n, (name, _) in enumerate(phases)}
+
+
+def bench_varlen(fa2, workloads, steps, warmup):
+    """Packed variable-length workload: fa2_fwd_varlen + fa2_bwd_varlen, timed with events."""
+    import torch
+    w = workloads.VARLEN_WORKLOADS[6]
+    t = workloads.varlen_workload_inputs(w)
+    lengths = [int(x) for x in t["lengths"]]
+    T, H, d = w.total, w.H, w.d
+    q, k, v, do = (t[n].cuda() for n in ("q", "k", "v", "dout"))
+    cu = t["cu_seqlens"].cuda()
+    out = torch.empty_like(q)
+    lse = torch.empty((H, T), dtype=torch.float32, device="cuda")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws_bytes = fa2.fa2_bwd_workspace_size(1, H, T, d)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    causal = int(w.causal)
+
+    def fwd():
+        fa2.fa2_fwd_varlen(q, k, v, out, lse, cu, w.nseq, T, H, d, w.scale, causal, -1, -1, None, sp)
+
+    def bwd():
+        fa2.fa2_bwd_varlen(q, k, v, out, lse, do, dq, dk, dv, cu, ws, ws_bytes, w.nseq, T, H, d, w.scale, causal,
+                           -1, -1, None, sp)
+
+    ms = timed([("fwd", fwd), ("bwd", bwd)], steps, warmup, stream)
+    f_fwd = sum(flops(1, H, n, d, w.causal)[0] for n in lengths)
+    f_bwd = 2.5 * f_fwd
+    fwd_tf = f_fwd / (ms["fwd"] * 1e-3) / 1e12
+    bwd_tf = f_bwd / (ms["bwd"] * 1e-3) / 1e12
+    step_tf = (f_fwd + f_bwd) / ((ms["fwd"] + ms["bwd"]) * 1e-3) / 1e12
+    return {
+        "workload": f"bf16 packed causal attention fwd+bwd, T={T} tokens in {w.nseq} sequences, H={H} d={d}",
+        "lengths": lengths,
+        "fwd_ms": round(ms["fwd"], 4),
+        "bwd_ms": round(ms["bwd"], 4),
+        "fwd_tflops": round(fwd_tf, 2),
+        "bwd_tflops": round(bwd_tf, 2),
+        "tflops": round(step_tf, 2),
+        "frac_of_peak": round(step_tf / PEAK_BF16_TFLOPS, 4),
+        "fwd_frac_of_peak": round(fwd_tf / PEAK_BF16_TFLOPS, 4),
+        "flop_convention": "per sequence: forward 4*H*n^2*d/2 (causal), backward 2.5x",
+    }
+
+
 def recorded_traffic(call):
     """HBM bytes per launch of the dominant kernel from the committed rocprofv3
     FETCH_SIZE / WRITE_SIZE passes (profiles/hbm_traffic.json), reported only if
@@ -90,6 +158,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-varlen", action="store_true", help="skip the packed variable-length measurement")
+    ap.add_argument("--varlen-only", action="store_true",
+                    help="only time the packed variable-length workload (prints its object as the JSON line)")
     ap.add_argument("--atomic-dq", action="store_true",
                     help="time the float-atomic dQ variant of the backward instead of the default passes")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -98,7 +169,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported (the path shards by "
-              f"(batch, head) with no exchange; see the design notes)", file=sys.stderr)
+              f"(batch, head) with no exchange, so one GPU's share is what this measures)", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -117,6 +188,9 @@ def main():
     import workloads
 
     fa2.load_library()
+    if args.varlen_only:
+        print(json.dumps({"varlen": bench_varlen(fa2, workloads, args.steps, args.warmup)}), flush=True)
+        return
     w = workloads.WORKLOADS[3]  # B=4, H=32, N=8192, d=128, causal
     B, H, N, d = w.B, w.H, w.N, w.d
     t = workloads.make_inputs(B, H, N, d, "bf16", seed=w.number, with_dout=True)
@@ -229,6 +303,8 @@ def main():
         "roofline": roofline,
         "kernels": kernels,
     }
+    if not args.no_varlen:
+        rec["varlen"] = bench_varlen(fa2, workloads, args.steps, args.warmup)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(rec), flush=True)

@@ -7,7 +7,8 @@ raises FA2Error; there is no fallback path.
 
 Low-level functions carry the C names and arguments (fa2_fwd, fa2_fwd_f32,
 fa2_bwd, fa2_bwd_workspace_size, fa2_bwd_prep, fa2_bwd_dkdv, fa2_bwd_dq,
-fa2_fwd_varlen, fa2_bwd_varlen, fa2_status_string, fa2_version); tensors or
+fa2_fwd_varlen, fa2_bwd_varlen, fa2_fwd_blocksparse, fa2_bwd_blocksparse,
+fa2_status_string, fa2_version); tensors or
 raw device addresses (int) are accepted for pointers. The convenience
 functions ``flash_attn_fwd`` / ``flash_attn_bwd`` mirror the parameter list of
 the FlashAttention v2 API on the wmrh.cn article (section 5.1) minus dropout:
@@ -15,7 +16,9 @@ softmax_scale=None (-> 1/sqrt(d)), causal, window_size=(-1, -1), alibi_slopes,
 and deterministic for the backward. ``flash_attn_varlen_fwd`` /
 ``flash_attn_varlen_bwd`` take sequences packed as [T, H, d] with int32
 boundaries ``cu_seqlens`` [B + 1] (variable-length batches, section 6 of the
-same article).
+same article). ``flash_attn_blocksparse_fwd`` / ``flash_attn_blocksparse_bwd``
+take a uint8 block mask over 128 x 128 blocks (block-sparse patterns, also
+section 6).
 """
 from __future__ import annotations
 
@@ -26,11 +29,14 @@ import os
 __all__ = [
     "FA2Error", "LIB_PATH", "load_library", "fa2_fwd", "fa2_fwd_f32", "fa2_bwd",
     "fa2_bwd_workspace_size", "fa2_bwd_prep", "fa2_bwd_dkdv", "fa2_bwd_dq", "fa2_fwd_varlen", "fa2_bwd_varlen",
-    "fa2_status_string", "fa2_version", "flash_attn_fwd", "flash_attn_bwd", "flash_attn_varlen_fwd",
-    "flash_attn_varlen_bwd", "FA2_OK", "FA2_ERR_INVALID_ARG", "FA2_ERR_UNSUPPORTED", "FA2_ERR_HIP",
+    "fa2_fwd_blocksparse", "fa2_bwd_blocksparse", "fa2_status_string", "fa2_version", "flash_attn_fwd",
+    "flash_attn_bwd", "flash_attn_varlen_fwd", "flash_attn_varlen_bwd", "flash_attn_blocksparse_fwd",
+    "flash_attn_blocksparse_bwd", "BLOCKSPARSE_BLOCK", "FA2_OK", "FA2_ERR_INVALID_ARG", "FA2_ERR_UNSUPPORTED", "FA2_ERR_HIP",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa2.so")
+
+BLOCKSPARSE_BLOCK = 128  # FA2_BLOCKSPARSE_BLOCK
 
 FA2_OK = 0
 FA2_ERR_INVALID_ARG = 1
@@ -42,6 +48,7 @@ _lib = None
 _P = ctypes.c_void_p
 _I = ctypes.c_int
 _F = ctypes.c_float
+_L = ctypes.c_longlong
 
 # C signatures of include/fa2.h
 SIGNATURES = {
@@ -56,6 +63,9 @@ SIGNATURES = {
     "fa2_fwd_varlen": ([_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _I, _I, _P, _P], _I),
     "fa2_bwd_varlen": ([_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _I, _I, _I, _I, _F, _I, _I, _I,
                         _P, _P], _I),
+    "fa2_fwd_blocksparse": ([_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _I, _I, _P, _P, _L, _L, _P], _I),
+    "fa2_bwd_blocksparse": ([_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _I, _I, _I, _I, _F, _I, _I, _I,
+                             _P, _P, _L, _L, _P], _I),
     "fa2_status_string": ([_I], ctypes.c_char_p),
     "fa2_version": ([], _I),
 }
@@ -187,6 +197,26 @@ def fa2_bwd_varlen(q, k, v, out, lse, dout, dq, dk, dv, cu_seqlens, workspace, w
     _check(st, "fa2_bwd_varlen")
 
 
+def fa2_fwd_blocksparse(q, k, v, out, lse, B, H, N, d, softmax_scale, causal, window_left, window_right,
+                        alibi_slopes, block_mask, mask_stride_b, mask_stride_h, stream=None):
+    st = load_library().fa2_fwd_blocksparse(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), int(B), int(H), int(N),
+                                            int(d), float(softmax_scale), int(causal), int(window_left),
+                                            int(window_right), _ptr(alibi_slopes), _ptr(block_mask),
+                                            int(mask_stride_b), int(mask_stride_h), _stream(stream))
+    _check(st, "fa2_fwd_blocksparse")
+
+
+def fa2_bwd_blocksparse(q, k, v, out, lse, dout, dq, dk, dv, workspace, workspace_bytes, B, H, N, d, softmax_scale,
+                        causal, window_left, window_right, alibi_slopes, block_mask, mask_stride_b, mask_stride_h,
+                        stream=None):
+    st = load_library().fa2_bwd_blocksparse(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dout), _ptr(dq),
+                                            _ptr(dk), _ptr(dv), _ptr(workspace), int(workspace_bytes), int(B), int(H),
+                                            int(N), int(d), float(softmax_scale), int(causal), int(window_left),
+                                            int(window_right), _ptr(alibi_slopes), _ptr(block_mask),
+                                            int(mask_stride_b), int(mask_stride_h), _stream(stream))
+    _check(st, "fa2_bwd_blocksparse")
+
+
 # ------------------------------------------------------------------ convenience wrappers
 
 def _check_tensors(*ts):
@@ -296,4 +326,58 @@ def flash_attn_varlen_bwd(dout, q, k, v, out, lse, cu_seqlens, softmax_scale=Non
     fa2_bwd_varlen(q, k, v, out, lse, dout, dq, dk, dv, cu, workspace, workspace.numel() * workspace.element_size(),
                    cu.numel() - 1, T, H, d, scale, int(bool(causal)), window_size[0], window_size[1],
                    _slopes(alibi_slopes, H, q.device))
+    return dq, dk, dv
+
+
+def _block_mask(block_mask, B, H, N, device):
+    """A uint8 mask [B or 1, H or 1, nb, nb] on the GPU -> (tensor, batch stride, head stride);
+    a size-1 batch or head dimension is shared (stride 0)."""
+    import torch
+    nb = -(-N // BLOCKSPARSE_BLOCK)
+    if not isinstance(block_mask, torch.Tensor) or block_mask.dtype != torch.uint8 or block_mask.dim() != 4:
+        raise FA2Error("block_mask must be a 4-D uint8 tensor [B or 1, H or 1, nb, nb]")
+    mb, mh, r, c = block_mask.shape
+    if (r, c) != (nb, nb) or mb not in (1, B) or mh not in (1, H):
+        raise FA2Error(f"block_mask shape {tuple(block_mask.shape)} does not fit B={B}, H={H}, nb={nb}")
+    if block_mask.device != device or block_mask.stride(3) != 1 or block_mask.stride(2) != nb:
+        raise FA2Error("block_mask must be on the tensors' GPU with contiguous [nb, nb] blocks")
+    sb = block_mask.stride(0) if mb == B and B > 1 else 0
+    sh = block_mask.stride(1) if mh == H and H > 1 else 0
+    return block_mask, sb, sh
+
+
+def flash_attn_blocksparse_fwd(q, k, v, block_mask, softmax_scale=None, causal=False, window_size=(-1, -1),
+                               alibi_slopes=None):
+    """Block-sparse forward. q, k, v: bf16 [B, N, H, d]; block_mask: uint8 [B or 1, H or 1, nb, nb]
+    over 128 x 128 blocks (non-zero = computed). Returns (out, lse [B, H, N])."""
+    import torch
+    _check_tensors(q, k, v)
+    if q.dtype != torch.bfloat16:
+        raise FA2Error("block-sparse attention takes bf16 tensors")
+    B, N, H, d = q.shape
+    m, sb, sh = _block_mask(block_mask, B, H, N, q.device)
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    out = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    fa2_fwd_blocksparse(q, k, v, out, lse, B, H, N, d, scale, int(bool(causal)), window_size[0], window_size[1],
+                        _slopes(alibi_slopes, H, q.device), m, sb, sh)
+    return out, lse
+
+
+def flash_attn_blocksparse_bwd(dout, q, k, v, out, lse, block_mask, softmax_scale=None, causal=False,
+                               window_size=(-1, -1), alibi_slopes=None, workspace=None):
+    """Block-sparse backward from the forward's out and lse. Returns (dq, dk, dv)."""
+    import torch
+    _check_tensors(q, k, v, out, dout)
+    if q.dtype != torch.bfloat16:
+        raise FA2Error("block-sparse attention takes bf16 tensors")
+    B, N, H, d = q.shape
+    m, sb, sh = _block_mask(block_mask, B, H, N, q.device)
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    if workspace is None:
+        workspace = torch.empty(max(fa2_bwd_workspace_size(B, H, N, d), 256), dtype=torch.uint8, device=q.device)
+    fa2_bwd_blocksparse(q, k, v, out, lse, dout, dq, dk, dv, workspace, workspace.numel() * workspace.element_size(),
+                        B, H, N, d, scale, int(bool(causal)), window_size[0], window_size[1],
+                        _slopes(alibi_slopes, H, q.device), m, sb, sh)
     return dq, dk, dv

@@ -29,6 +29,11 @@
 // VARLEN (packed sequences of different lengths, deterministic variant only):
 // as in the forward, workgroups cover an upper bound of the blocks present and
 // find their sequence with varlen_block; D and LSE are [H, total tokens].
+// SPARSE (128 x 128 block mask, deterministic variant only): each workgroup
+// compacts the tiles of its active blocks into an LDS list and streams only
+// those. In the key-block pass a list entry also carries which of the
+// workgroup's (up to two) key blocks are active for that query tile, and a
+// wave whose key block is off skips the tile's compute.
 #include <type_traits>
 
 #include "common.hpp"
@@ -142,10 +147,12 @@ __device__ __forceinline__ bool bwd_sequence(const BwdParams& p, int rows, bool 
   return true;
 }
 
-template <int D, bool ALIBI, bool DET, int NW, int NST, bool VARLEN>
+template <int D, bool ALIBI, bool DET, int NW, int NST, bool VARLEN, bool SPARSE>
 __global__ __launch_bounds__(NW * 64, ((D == 128 && !DET) ? 4 : 8) / NW) void bwd_main_kernel(BwdParams p) {
-  static_assert(DET || !VARLEN, "packed batches use the split dQ pass");
+  static_assert(DET || !(VARLEN || SPARSE), "packed and block-sparse batches use the split dQ pass");
+  static_assert(!(VARLEN && SPARSE), "packed batches have no block mask");
   using S = BwdShape<D, NW, NST, DET>;
+  static_assert(!SPARSE || (S::BK % kSparseBlock == 0 && S::BK <= 2 * kSparseBlock), "one or two key blocks");
   constexpr int ROWB = 2 * D;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   char* k_lds = smem;
@@ -187,6 +194,29 @@ __global__ __launch_bounds__(NW * 64, ((D == 128 && !DET) ? 4 : 8) / NW) void bw
   if (p.wr >= 0) q_lo = max(0, k0 - p.wr);
   if (p.wl >= 0) q_hi = min(N - 1, k_last + p.wl);
   const int it_lo = q_lo / S::BQ, it_hi = q_hi / S::BQ + 1;
+
+  // The query tiles to visit: it_lo .. it_hi - 1, or for SPARSE those of active
+  // blocks, each with a bit per key block of this workgroup (bit 0: keys k0 ..
+  // k0 + 127, bit 1: the next 128).
+  uint16_t* tile_list = reinterpret_cast<uint16_t*>(smem + S::LDS);
+  int n_tiles = it_hi - it_lo;
+  if constexpr (SPARSE) {
+    const uint8_t* mbh = p.block_mask + (tok0 / N) * p.mask_sb + (int64_t)h * p.mask_sh;
+    const int c0 = k0 / kSparseBlock;
+    const bool two = S::BK > kSparseBlock && c0 + 1 < p.nbk;
+    n_tiles = compact_tiles(tile_list, it_lo, it_hi, w, [&](int it) -> uint32_t {
+      const uint8_t* row = mbh + (int64_t)((it * S::BQ) / kSparseBlock) * p.nbk + c0;
+      return (row[0] != 0 ? 1u : 0u) | (two && row[1] != 0 ? 2u : 0u);
+    });
+    __syncthreads();
+  }
+  auto entry_at = [&](int u) __attribute__((always_inline)) -> uint32_t {
+    if constexpr (SPARSE) {
+      return __builtin_amdgcn_readfirstlane((uint32_t)tile_list[u]);
+    } else {
+      return (uint32_t)(it_lo + u);
+    }
+  };
 
   // Per-lane LDS bases; every read below is base ^ constant or base + constant.
   const int ar = kperm(l32);  // A-operand row (query) for S and dP
@@ -260,17 +290,22 @@ __global__ __launch_bounds__(NW * 64, ((D == 128 && !DET) ? 4 : 8) / NW) void bw
     }
   };
 
-  // One 32-query block; the stage is a compile-time constant.
-  auto body = [&](int it, auto stage_c) __attribute__((always_inline)) {
+  // One 32-query block (the u-th to visit); the stage is a compile-time constant.
+  auto body = [&](int u, auto stage_c) __attribute__((always_inline)) {
     constexpr int stg = decltype(stage_c)::value;
-    if (it + NST - 1 < it_hi) issue_q(it + NST - 1, std::integral_constant<int, (stg + NST - 1) % NST>{});
+    if (u + NST - 1 < n_tiles)
+      issue_q((int)(entry_at(u + NST - 1) & kTileIndexMask), std::integral_constant<int, (stg + NST - 1) % NST>{});
     opaque(qa_base);
     opaque(kb_base);
     opaque(tr_lo);
     opaque(tr_hi);
+    const uint32_t ent = entry_at(u);
+    const int it = (int)(ent & kTileIndexMask);
     const int i0 = it * S::BQ;
     const int i1 = i0 + S::BQ - 1;
-    const bool skip = kw0 >= N || (p.wr >= 0 && i1 + p.wr < kw0) || (p.wl >= 0 && i0 - p.wl > kw0 + 31);
+    // SPARSE: this wave's key block (32 keys per wave, 128 per block) must be active
+    const bool off = SPARSE && ((ent >> 14) & (1u << ((32 * w) / kSparseBlock))) == 0;
+    const bool skip = off || kw0 >= N || (p.wr >= 0 && i1 + p.wr < kw0) || (p.wl >= 0 && i0 - p.wl > kw0 + 31);
     if (!skip) {
       const char* q_t = stage_lds + stg * S::STAGE_BYTES;
       const char* do_t = q_t + S::QT_BYTES;
@@ -386,13 +421,13 @@ __global__ __launch_bounds__(NW * 64, ((D == 128 && !DET) ? 4 : 8) / NW) void bw
 
   static_for<0, NST - 1>([&](auto sc) {
     constexpr int k = decltype(sc)::value;
-    if (it_lo + k < it_hi) issue_q(it_lo + k, std::integral_constant<int, k>{});
+    if (k < n_tiles) issue_q((int)(entry_at(k) & kTileIndexMask), std::integral_constant<int, k>{});
   });
   wait_next();
-  for (int it = it_lo; it < it_hi; it += NST) {
+  for (int u = 0; u < n_tiles; u += NST) {
     static_for<0, NST>([&](auto sc) {
       constexpr int k = decltype(sc)::value;
-      if (it + k < it_hi) body(it + k, sc);
+      if (u + k < n_tiles) body(u + k, sc);
     });
   }
 
@@ -423,8 +458,10 @@ __global__ __launch_bounds__(NW * 64, ((D == 128 && !DET) ? 4 : 8) / NW) void bw
 // dP^T = V dO^T put one query per lane (column), so LSE and D are per-lane
 // scalars, and dS^T feeds dQ^T += K^T dS^T as the B operand straight from
 // registers (K^T read transposed from the K tile).
-template <int D, bool ALIBI, int NW, int NST, bool VARLEN>
+template <int D, bool ALIBI, int NW, int NST, bool VARLEN, bool SPARSE>
 __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq_det_kernel(BwdParams p) {
+  static_assert(!(VARLEN && SPARSE), "packed batches have no block mask");
+  static_assert(!SPARSE || NW * 32 == kSparseBlock, "a workgroup covers one mask row");
   constexpr int BR = NW * 32, BC = 32;
   constexpr int KS = D / 16, MB = D / 32;
   constexpr int ROWB = 2 * D;
@@ -470,6 +507,23 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq_det_kernel(BwdParams p
   if (p.wr >= 0) kv_hi = min(N, q_last + p.wr + 1);
   const int t_lo = kv_lo / BC, t_hi = (kv_hi + BC - 1) / BC;
 
+  // The key tiles to visit: t_lo .. t_hi - 1, or for SPARSE those of active key blocks.
+  uint16_t* tile_list = reinterpret_cast<uint16_t*>(smem + NST * STAGE);
+  int n_tiles = t_hi - t_lo;
+  if constexpr (SPARSE) {
+    const uint8_t* mrow = p.block_mask + (tok0 / N) * p.mask_sb + (int64_t)h * p.mask_sh + (int64_t)qb * p.nbk;
+    n_tiles = compact_tiles(tile_list, t_lo, t_hi, w,
+                            [&](int t) -> uint32_t { return mrow[(t * BC) / kSparseBlock] != 0 ? 1u : 0u; });
+    __syncthreads();
+  }
+  auto tile_at = [&](int u) __attribute__((always_inline)) -> int {
+    if constexpr (SPARSE) {
+      return __builtin_amdgcn_readfirstlane((int)(tile_list[u] & kTileIndexMask));
+    } else {
+      return t_lo + u;
+    }
+  };
+
   uint32_t dma_off[PER_WAVE];
 #pragma unroll
   for (int n = 0; n < PER_WAVE; ++n) {
@@ -509,9 +563,10 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq_det_kernel(BwdParams p
     }
   };
 
-  auto body = [&](int t, auto stage_c) __attribute__((always_inline)) {
+  auto body = [&](int u, auto stage_c) __attribute__((always_inline)) {
     constexpr int st = decltype(stage_c)::value;
-    if (t + NST - 1 < t_hi) issue(t + NST - 1, std::integral_constant<int, (st + NST - 1) % NST>{});
+    if (u + NST - 1 < n_tiles) issue(tile_at(u + NST - 1), std::integral_constant<int, (st + NST - 1) % NST>{});
+    const int t = tile_at(u);
     opaque(abase);
     opaque(tr_lo);
     opaque(tr_hi);
@@ -572,13 +627,13 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq_det_kernel(BwdParams p
 
   static_for<0, NST - 1>([&](auto sc) {
     constexpr int k = decltype(sc)::value;
-    if (t_lo + k < t_hi) issue(t_lo + k, std::integral_constant<int, k>{});
+    if (k < n_tiles) issue(tile_at(k), std::integral_constant<int, k>{});
   });
   wait_vm_and_sync<2 * PER_WAVE * (NST - 2)>();
-  for (int t = t_lo; t < t_hi; t += NST) {
+  for (int u = 0; u < n_tiles; u += NST) {
     static_for<0, NST>([&](auto sc) {
       constexpr int k = decltype(sc)::value;
-      if (t + k < t_hi) body(t + k, sc);
+      if (u + k < n_tiles) body(u + k, sc);
     });
   }
   if (!wave_live || qi >= N) return;
@@ -625,33 +680,35 @@ static hipError_t launch_prep_d(const BwdParams& p, bool zero_acc, hipStream_t s
 }
 
 // Pass 2: the key-block pass (dK, dV; with DET = false also the atomic dQ).
-template <int D, bool ALIBI, bool DET, bool VARLEN>
+template <int D, bool ALIBI, bool DET, bool VARLEN, bool SPARSE>
 static hipError_t launch_main_d(const BwdParams& p0, hipStream_t stream) {
   // Split dQ pass (DET): deeper Q/dO ring and 8 waves per key block; atomic dQ:
   // 4 waves, 2 stages (its dS^T buffer and dQ step need the room).
   constexpr int NW = DET ? (D == 128 ? FA2_BWD_NW : 4) : 4;
   constexpr int NST = DET ? (D == 128 ? FA2_BWD_NST : 3) : 2;
   using S = BwdShape<D, NW, NST, DET>;
-  auto kmain = bwd_main_kernel<D, ALIBI, DET, NW, NST, VARLEN>;
+  auto kmain = bwd_main_kernel<D, ALIBI, DET, NW, NST, VARLEN, SPARSE>;
+  constexpr int lds = S::LDS + (SPARSE ? 2 * (kSparseMaxN / S::BQ) : 0);  // + the query-tile list
+  static_assert(lds <= 160 * 1024, "LDS budget");
   static bool main_attr = false;
   hipError_t e;
   if (!main_attr) {
-    if ((e = set_lds(kmain, S::LDS)) != hipSuccess) return e;
+    if ((e = set_lds(kmain, lds)) != hipSuccess) return e;
     main_attr = true;
   }
   BwdParams p = p0;
   p.nblk = VARLEN ? (int)varlen_block_bound(p.N, p.nseq, S::BK) : (p.N + S::BK - 1) / S::BK;
-  hipLaunchKernelGGL(kmain, dim3((unsigned)((int64_t)p.nblk * p.B * p.H)), dim3(S::NT), S::LDS, stream, p);
+  hipLaunchKernelGGL(kmain, dim3((unsigned)((int64_t)p.nblk * p.B * p.H)), dim3(S::NT), lds, stream, p);
   return hipGetLastError();
 }
 
 // Pass 3 of the split backward: dQ by a sweep over key tiles per query block.
-template <int D, bool ALIBI, bool VARLEN>
+template <int D, bool ALIBI, bool VARLEN, bool SPARSE>
 static hipError_t launch_dq_d(const BwdParams& p0, hipStream_t stream) {
   constexpr int DNW = D == 128 ? FA2_DQ_NW : 4;
   constexpr int DNST = FA2_DQ_NST;
-  auto kdq = bwd_dq_det_kernel<D, ALIBI, DNW, DNST, VARLEN>;
-  constexpr int DQ_LDS = DNST * 2 * 32 * D * 2;
+  auto kdq = bwd_dq_det_kernel<D, ALIBI, DNW, DNST, VARLEN, SPARSE>;
+  constexpr int DQ_LDS = DNST * 2 * 32 * D * 2 + (SPARSE ? 2 * (kSparseMaxN / 32) : 0);  // ring (+ tile list)
   static bool dq_attr = false;
   hipError_t e;
   if (!dq_attr) {
@@ -677,27 +734,38 @@ hipError_t launch_bwd_prep(const BwdParams& p, int d, bool zero_acc, hipStream_t
   return d == 128 ? launch_prep_d<128>(p, zero_acc, stream) : launch_prep_d<64>(p, zero_acc, stream);
 }
 
-template <int D, bool VARLEN>
+template <int D, bool VARLEN, bool SPARSE>
 static hipError_t launch_dkdv_v(const BwdParams& p, hipStream_t stream) {
-  return p.alibi != nullptr ? launch_main_d<D, true, true, VARLEN>(p, stream)
-                            : launch_main_d<D, false, true, VARLEN>(p, stream);
+  return p.alibi != nullptr ? launch_main_d<D, true, true, VARLEN, SPARSE>(p, stream)
+                            : launch_main_d<D, false, true, VARLEN, SPARSE>(p, stream);
 }
 
-template <int D, bool VARLEN>
+template <int D, bool VARLEN, bool SPARSE>
 static hipError_t launch_dq_v(const BwdParams& p, hipStream_t stream) {
-  return p.alibi != nullptr ? launch_dq_d<D, true, VARLEN>(p, stream) : launch_dq_d<D, false, VARLEN>(p, stream);
+  return p.alibi != nullptr ? launch_dq_d<D, true, VARLEN, SPARSE>(p, stream)
+                            : launch_dq_d<D, false, VARLEN, SPARSE>(p, stream);
+}
+
+template <int D>
+static hipError_t launch_dkdv_mode(const BwdParams& p, hipStream_t stream) {
+  if (p.block_mask != nullptr) return launch_dkdv_v<D, false, true>(p, stream);
+  if (p.cu_seqlens != nullptr) return launch_dkdv_v<D, true, false>(p, stream);
+  return launch_dkdv_v<D, false, false>(p, stream);
+}
+
+template <int D>
+static hipError_t launch_dq_mode(const BwdParams& p, hipStream_t stream) {
+  if (p.block_mask != nullptr) return launch_dq_v<D, false, true>(p, stream);
+  if (p.cu_seqlens != nullptr) return launch_dq_v<D, true, false>(p, stream);
+  return launch_dq_v<D, false, false>(p, stream);
 }
 
 hipError_t launch_bwd_dkdv(const BwdParams& p, int d, hipStream_t stream) {
-  const bool varlen = p.cu_seqlens != nullptr;
-  if (d == 128) return varlen ? launch_dkdv_v<128, true>(p, stream) : launch_dkdv_v<128, false>(p, stream);
-  return varlen ? launch_dkdv_v<64, true>(p, stream) : launch_dkdv_v<64, false>(p, stream);
+  return d == 128 ? launch_dkdv_mode<128>(p, stream) : launch_dkdv_mode<64>(p, stream);
 }
 
 hipError_t launch_bwd_dq(const BwdParams& p, int d, hipStream_t stream) {
-  const bool varlen = p.cu_seqlens != nullptr;
-  if (d == 128) return varlen ? launch_dq_v<128, true>(p, stream) : launch_dq_v<128, false>(p, stream);
-  return varlen ? launch_dq_v<64, true>(p, stream) : launch_dq_v<64, false>(p, stream);
+  return d == 128 ? launch_dq_mode<128>(p, stream) : launch_dq_mode<64>(p, stream);
 }
 
 hipError_t launch_bwd_bf16(const BwdParams& p, int d, bool split_dq, hipStream_t stream) {
@@ -707,13 +775,15 @@ hipError_t launch_bwd_bf16(const BwdParams& p, int d, bool split_dq, hipStream_t
     if ((e = launch_bwd_dkdv(p, d, stream)) != hipSuccess) return e;
     return launch_bwd_dq(p, d, stream);
   }
-  if (p.cu_seqlens != nullptr) return hipErrorInvalidValue;  // packed batches: split dQ only
+  if (p.cu_seqlens != nullptr || p.block_mask != nullptr) return hipErrorInvalidValue;  // split dQ only
   if ((e = launch_bwd_prep(p, d, true, stream)) != hipSuccess) return e;
   const bool alibi = p.alibi != nullptr;
   if (d == 128) {
-    e = alibi ? launch_main_d<128, true, false, false>(p, stream) : launch_main_d<128, false, false, false>(p, stream);
+    e = alibi ? launch_main_d<128, true, false, false, false>(p, stream)
+              : launch_main_d<128, false, false, false, false>(p, stream);
   } else {
-    e = alibi ? launch_main_d<64, true, false, false>(p, stream) : launch_main_d<64, false, false, false>(p, stream);
+    e = alibi ? launch_main_d<64, true, false, false, false>(p, stream)
+              : launch_main_d<64, false, false, false, false>(p, stream);
   }
   if (e != hipSuccess) return e;
   return d == 128 ? launch_convert_d<128>(p, stream) : launch_convert_d<64>(p, stream);

@@ -245,6 +245,36 @@ __host__ __device__ inline int64_t varlen_block_bound(int total, int nseq, int r
   return ((int64_t)total + (int64_t)nseq * (rows - 1)) / rows;
 }
 
+// Block-sparse attention: one mask byte per (query block, key block) pair of
+// kSparseBlock x kSparseBlock positions; zero means the pair is skipped.
+constexpr int kSparseBlock = 128;
+constexpr int kSparseMaxN = 65536;  // bounds the per-workgroup tile list kept in LDS
+
+// Number of lanes below this one whose bit is set in a wave-wide ballot.
+__device__ __forceinline__ int lanes_below(uint64_t bal) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0));
+}
+
+// Compacts the tiles t in [t_lo, t_hi) whose flags (keep(t), two bits) are not
+// zero into list[0 .. n) as t | flags << 14 (LDS, in increasing t; wave 0
+// writes) and returns n. Tile indices must stay below 2^14. Every wave
+// evaluates the same predicates, so n is uniform without a broadcast; the
+// caller synchronises the workgroup before reading the list.
+template <typename F>
+__device__ __forceinline__ int compact_tiles(uint16_t* list, int t_lo, int t_hi, int w, F&& keep) {
+  const int lane = threadIdx.x & 63;
+  int n = 0;
+  for (int t0 = t_lo; t0 < t_hi; t0 += 64) {
+    const int t = t0 + lane;
+    const uint32_t f = t < t_hi ? (keep(t) & 3u) : 0u;
+    const uint64_t bal = __builtin_amdgcn_ballot_w64(f != 0);
+    if (w == 0 && f != 0) list[n + lanes_below(bal)] = (uint16_t)(t | (f << 14));
+    n += __builtin_popcountll(bal);
+  }
+  return n;
+}
+constexpr uint32_t kTileIndexMask = (1u << 14) - 1;
+
 struct FwdParams {
   const void* q;
   const void* k;
@@ -256,6 +286,9 @@ struct FwdParams {
   int n_qblocks;     // query blocks per head (packed batches: the virtual-block bound)
   const int* cu_seqlens;  // [nseq + 1] sequence boundaries of a packed batch, or null
   int nseq;
+  const uint8_t* block_mask;  // block-sparse: mask bytes, or null
+  int64_t mask_sb, mask_sh;   // block-sparse: element strides between batches / heads
+  int nbk;                    // block-sparse: blocks per side, ceil(N / kSparseBlock)
   float scale;       // softmax scale
   float scale_log2;  // softmax scale * log2(e)
   int causal;
@@ -280,6 +313,9 @@ struct BwdParams {
   int nblk;          // blocks per head of the kernel being launched (packed: virtual-block bound)
   const int* cu_seqlens;  // [nseq + 1] sequence boundaries of a packed batch, or null
   int nseq;
+  const uint8_t* block_mask;  // block-sparse: mask bytes, or null
+  int64_t mask_sb, mask_sh;
+  int nbk;
   float scale;
   float scale_log2;
   int causal;

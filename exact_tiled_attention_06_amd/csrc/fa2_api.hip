@@ -253,6 +253,65 @@ fa2_status_t fa2_bwd_varlen(const void* q, const void* k, const void* v, const v
   return hip_status(fa2::launch_bwd_bf16(p, d, true, (hipStream_t)stream));
 }
 
+}  // extern "C"
+
+namespace {
+
+// Checks shared by the block-sparse entry points (after the dense checks).
+fa2_status_t check_block_mask(const unsigned char* block_mask, int N, long long stride_b, long long stride_h) {
+  if (N > fa2::kSparseMaxN) return FA2_ERR_UNSUPPORTED;
+  if (!block_mask || stride_b < 0 || stride_h < 0) return FA2_ERR_INVALID_ARG;
+  return FA2_OK;
+}
+
+template <typename P>
+void set_block_mask(P* p, const unsigned char* block_mask, int N, long long stride_b, long long stride_h) {
+  p->block_mask = block_mask;
+  p->mask_sb = stride_b;
+  p->mask_sh = stride_h;
+  p->nbk = (N + fa2::kSparseBlock - 1) / fa2::kSparseBlock;
+}
+
+}  // namespace
+
+extern "C" {
+
+fa2_status_t fa2_fwd_blocksparse(const void* q, const void* k, const void* v, void* out, float* lse, int B, int H,
+                                 int N, int d, float softmax_scale, int causal, int window_left, int window_right,
+                                 const float* alibi_slopes, const unsigned char* block_mask,
+                                 long long mask_stride_b, long long mask_stride_h, void* stream) {
+  bool empty = false;
+  fa2_status_t st = check_common(B, H, N, d, softmax_scale, window_left, window_right, &empty);
+  if (st != FA2_OK || empty) return st;
+  if ((st = check_block_mask(block_mask, N, mask_stride_b, mask_stride_h)) != FA2_OK) return st;
+  if (!q || !k || !v || !out || !lse) return FA2_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(lse))
+    return FA2_ERR_INVALID_ARG;
+  if (alibi_slopes && !aligned4(alibi_slopes)) return FA2_ERR_INVALID_ARG;
+  fa2::FwdParams p = fwd_params(q, k, v, out, lse, B, H, N, softmax_scale, causal, window_left, window_right,
+                                alibi_slopes);
+  set_block_mask(&p, block_mask, N, mask_stride_b, mask_stride_h);
+  return hip_status(fa2::launch_fwd_bf16(p, d, (hipStream_t)stream));
+}
+
+fa2_status_t fa2_bwd_blocksparse(const void* q, const void* k, const void* v, const void* out, const float* lse,
+                                 const void* dout, void* dq, void* dk, void* dv, void* workspace,
+                                 size_t workspace_bytes, int B, int H, int N, int d, float softmax_scale,
+                                 int causal, int window_left, int window_right, const float* alibi_slopes,
+                                 const unsigned char* block_mask, long long mask_stride_b,
+                                 long long mask_stride_h, void* stream) {
+  fa2::BwdParams p;
+  bool empty = false;
+  fa2_status_t st = check_common(B, H, N, d, softmax_scale, window_left, window_right, &empty);
+  if (st != FA2_OK || empty) return st;
+  if ((st = check_block_mask(block_mask, N, mask_stride_b, mask_stride_h)) != FA2_OK) return st;
+  st = bwd_setup(q, k, v, out, lse, dout, dq, dk, dv, workspace, workspace_bytes, delta_bytes(B, H, N), B, H, N, d,
+                 softmax_scale, causal, window_left, window_right, alibi_slopes, true, true, true, true, &p, &empty);
+  if (st != FA2_OK || empty) return st;
+  set_block_mask(&p, block_mask, N, mask_stride_b, mask_stride_h);
+  return hip_status(fa2::launch_bwd_bf16(p, d, true, (hipStream_t)stream));
+}
+
 const char* fa2_status_string(fa2_status_t s) {
   switch (s) {
     case FA2_OK: return "FA2_OK";

@@ -38,6 +38,12 @@
 //    boundaries (varlen_block) and the few spare workgroups exit at once.
 //    Everything after that is the fixed-length code with the sequence's start,
 //    length and LSE row.
+//  * SPARSE: block-sparse attention (the block-sparse patterns of the same
+//    article, section 6) with a byte per 128 x 128 (query block, key block)
+//    pair. The workgroup's query block is one mask row; the K/V tiles of its
+//    active key blocks are compacted into a list in LDS (compact_tiles) and
+//    the ring streams only those, so skipped blocks cost neither loads nor
+//    MFMAs. Masks inside a tile are the dense ones.
 #include <type_traits>
 
 #include "common.hpp"
@@ -66,9 +72,11 @@ struct FwdShape {
   static constexpr int ROWB = 2 * D;        // bytes per LDS row
 };
 
-template <int D, int NW, int BC, int NST, bool ALIBI, bool VARLEN>
+template <int D, int NW, int BC, int NST, bool ALIBI, bool VARLEN, bool SPARSE>
 __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(FwdParams p) {
   using S = FwdShape<D, NW, BC, NST>;
+  static_assert(!(VARLEN && SPARSE), "packed batches have no block mask");
+  static_assert(!SPARSE || S::BR == kSparseBlock, "a workgroup covers one mask row");
   constexpr int PER_WAVE = S::PER_WAVE;
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
@@ -122,6 +130,24 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(FwdParams p) 
   if (p.wr >= 0) kv_hi = min(N, q_last + p.wr + 1);
   const int t_lo = kv_lo / BC, t_hi = (kv_hi + BC - 1) / BC;
 
+  // The tiles to visit: t_lo .. t_hi - 1, or for SPARSE those of active key blocks.
+  uint16_t* tile_list = reinterpret_cast<uint16_t*>(smem + S::LDS);
+  int n_tiles = t_hi - t_lo;
+  if constexpr (SPARSE) {
+    const uint8_t* mrow = p.block_mask + (int64_t)(bh / p.H) * p.mask_sb + (int64_t)h * p.mask_sh +
+                          (int64_t)qb * p.nbk;
+    n_tiles = compact_tiles(tile_list, t_lo, t_hi, w,
+                            [&](int t) -> uint32_t { return mrow[(t * BC) / kSparseBlock] != 0 ? 1u : 0u; });
+    __syncthreads();
+  }
+  auto tile_at = [&](int u) __attribute__((always_inline)) -> int {
+    if constexpr (SPARSE) {
+      return __builtin_amdgcn_readfirstlane((int)(tile_list[u] & kTileIndexMask));
+    } else {
+      return t_lo + u;
+    }
+  };
+
   // Per-lane byte offsets of this lane's direct-load pieces, relative to a tile's first row.
   uint32_t dma_off[PER_WAVE];
 #pragma unroll
@@ -168,11 +194,12 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(FwdParams p) 
     }
   };
 
-  // One tile of the online softmax for this wave; the stage is a compile-time constant.
-  // Tile t + NST - 1 is issued into the stage freed by tile t - 1.
-  auto body = [&](int t, auto stage_c) __attribute__((always_inline)) {
+  // One tile (the u-th to visit) of the online softmax for this wave; the stage is a
+  // compile-time constant. Tile u + NST - 1 is issued into the stage freed by tile u - 1.
+  auto body = [&](int u, auto stage_c) __attribute__((always_inline)) {
     constexpr int st = decltype(stage_c)::value;
-    if (t + NST - 1 < t_hi) issue(t + NST - 1, std::integral_constant<int, (st + NST - 1) % NST>{});
+    if (u + NST - 1 < n_tiles) issue(tile_at(u + NST - 1), std::integral_constant<int, (st + NST - 1) % NST>{});
+    const int t = tile_at(u);
     opaque(kbase);
     opaque(vbase_lo);
     opaque(vbase_hi);
@@ -275,13 +302,13 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(FwdParams p) 
 
   static_for<0, NST - 1>([&](auto sc) {
     constexpr int k = decltype(sc)::value;
-    if (t_lo + k < t_hi) issue(t_lo + k, std::integral_constant<int, k>{});
+    if (k < n_tiles) issue(tile_at(k), std::integral_constant<int, k>{});
   });
   wait_vm_and_sync<S::VM_PER_TILE * (NST - 2)>();
-  for (int t = t_lo; t < t_hi; t += NST) {
+  for (int u = 0; u < n_tiles; u += NST) {
     static_for<0, NST>([&](auto sc) {
       constexpr int k = decltype(sc)::value;
-      if (t + k < t_hi) body(t + k, sc);
+      if (u + k < n_tiles) body(u + k, sc);
     });
   }
 
@@ -306,20 +333,22 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(FwdParams p) 
   }
 }
 
-template <int D, int NW, int BC, int NST, bool ALIBI, bool VARLEN>
+template <int D, int NW, int BC, int NST, bool ALIBI, bool VARLEN, bool SPARSE>
 static hipError_t launch_fwd_cfg(const FwdParams& p0, hipStream_t stream) {
   using S = FwdShape<D, NW, BC, NST>;
   FwdParams p = p0;
   p.n_qblocks = VARLEN ? (int)varlen_block_bound(p.N, p.nseq, S::BR) : (p.N + S::BR - 1) / S::BR;
-  auto kern = fwd_bf16_kernel<D, NW, BC, NST, ALIBI, VARLEN>;
+  auto kern = fwd_bf16_kernel<D, NW, BC, NST, ALIBI, VARLEN, SPARSE>;
+  // SPARSE: room for the tile list after the ring (one uint16 per key tile)
+  constexpr int lds = S::LDS + (SPARSE ? 2 * (kSparseMaxN / BC) : 0);
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, S::LDS);
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   const int64_t nblk = (int64_t)p.n_qblocks * p.B * p.H;
-  hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3(S::NT), S::LDS, stream, p);
+  hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3(S::NT), lds, stream, p);
   return hipGetLastError();
 }
 
@@ -330,17 +359,22 @@ static hipError_t launch_fwd_cfg(const FwdParams& p0, hipStream_t stream) {
 #define FA2_FWD_NST 2
 #endif
 
-template <int D, bool VARLEN>
+template <int D, bool VARLEN, bool SPARSE>
 static hipError_t launch_fwd_d(const FwdParams& p, hipStream_t stream) {
   constexpr int NW = FA2_FWD_NW, NST = FA2_FWD_NST;
-  return p.alibi != nullptr ? launch_fwd_cfg<D, NW, 64, NST, true, VARLEN>(p, stream)
-                            : launch_fwd_cfg<D, NW, 64, NST, false, VARLEN>(p, stream);
+  return p.alibi != nullptr ? launch_fwd_cfg<D, NW, 64, NST, true, VARLEN, SPARSE>(p, stream)
+                            : launch_fwd_cfg<D, NW, 64, NST, false, VARLEN, SPARSE>(p, stream);
+}
+
+template <int D>
+static hipError_t launch_fwd_mode(const FwdParams& p, hipStream_t stream) {
+  if (p.block_mask != nullptr) return launch_fwd_d<D, false, true>(p, stream);
+  if (p.cu_seqlens != nullptr) return launch_fwd_d<D, true, false>(p, stream);
+  return launch_fwd_d<D, false, false>(p, stream);
 }
 
 hipError_t launch_fwd_bf16(const FwdParams& p, int d, hipStream_t stream) {
-  const bool varlen = p.cu_seqlens != nullptr;
-  if (d == 128) return varlen ? launch_fwd_d<128, true>(p, stream) : launch_fwd_d<128, false>(p, stream);
-  return varlen ? launch_fwd_d<64, true>(p, stream) : launch_fwd_d<64, false>(p, stream);
+  return d == 128 ? launch_fwd_mode<128>(p, stream) : launch_fwd_mode<64>(p, stream);
 }
 
 }  // namespace fa2

@@ -182,6 +182,42 @@ fa2_status_t fa2_bwd_varlen(const void* q, const void* k, const void* v, const v
                             int window_left, int window_right, const float* alibi_slopes,
                             void* stream);
 
+/*
+ * Block-sparse attention. The wmrh.cn FlashAttention v2 article (section 6,
+ * future directions) suggests combining the method with block-sparse
+ * patterns; the page fixes no format, so this one is:
+ *   - the sequence is cut into blocks of FA2_BLOCKSPARSE_BLOCK = 128
+ *     positions, nb = ceil(N / 128) per side;
+ *   - block_mask: DEVICE bytes; the byte of (batch b, head h, query block r,
+ *     key block c) is block_mask[b * mask_stride_b + h * mask_stride_h +
+ *     r * nb + c] (strides in bytes, >= 0; 0 shares one mask across batches or
+ *     heads). Non-zero: the block pair is computed; zero: it is skipped;
+ *   - key j is visible to query i iff the dense rule (causal, window) allows
+ *     it AND the byte of (i / 128, j / 128) is non-zero; ALiBi is unchanged;
+ *   - a query row left with no visible key gets O = 0, LSE = -inf and zero
+ *     gradients (its dO contributes nothing).
+ * Skipped blocks cost neither memory traffic nor matrix work: each workgroup
+ * compacts the tiles of its active blocks and streams only those.
+ * Layouts, other arguments and errors as for fa2_fwd / fa2_bwd. N above 65536
+ * is FA2_ERR_UNSUPPORTED; a null block_mask or a negative stride is
+ * FA2_ERR_INVALID_ARG. The backward is always the atomic-free algorithm
+ * (bitwise repeatable) and needs round_up(4 * B * H * N, 256) workspace bytes.
+ */
+#define FA2_BLOCKSPARSE_BLOCK 128
+
+fa2_status_t fa2_fwd_blocksparse(const void* q, const void* k, const void* v, void* out, float* lse,
+                                 int B, int H, int N, int d, float softmax_scale, int causal,
+                                 int window_left, int window_right, const float* alibi_slopes,
+                                 const unsigned char* block_mask, long long mask_stride_b,
+                                 long long mask_stride_h, void* stream);
+
+fa2_status_t fa2_bwd_blocksparse(const void* q, const void* k, const void* v, const void* out,
+                                 const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                                 void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
+                                 float softmax_scale, int causal, int window_left, int window_right,
+                                 const float* alibi_slopes, const unsigned char* block_mask,
+                                 long long mask_stride_b, long long mask_stride_h, void* stream);
+
 /* Static, human-readable name of a status code. */
 const char* fa2_status_string(fa2_status_t status);
 

@@ -21,3 +21,9 @@ from .varlen import (  # noqa: F401
     varlen_forward,
     varlen_forward_rows,
 )
+from .blocksparse import (  # noqa: F401
+    blocksparse_backward,
+    blocksparse_backward_sampled,
+    blocksparse_forward,
+    blocksparse_forward_rows,
+)

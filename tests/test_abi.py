@@ -32,7 +32,8 @@ def lib():
 def test_header_declares_the_documented_entry_points():
     assert header_functions() == sorted(
         ["fa2_fwd", "fa2_fwd_f32", "fa2_bwd", "fa2_bwd_workspace_size", "fa2_bwd_prep", "fa2_bwd_dkdv",
-         "fa2_bwd_dq", "fa2_fwd_varlen", "fa2_bwd_varlen", "fa2_status_string", "fa2_version"])
+         "fa2_bwd_dq", "fa2_fwd_varlen", "fa2_bwd_varlen", "fa2_fwd_blocksparse", "fa2_bwd_blocksparse",
+         "fa2_status_string", "fa2_version"])
 
 
 def test_library_exports_every_header_symbol(lib):
@@ -197,6 +198,49 @@ def test_varlen_backward_checks_workspace_and_gradients(lib):
 def test_varlen_empty_problem_is_ok_and_launches_nothing(lib, over):
     assert lib.fa2_fwd_varlen(*varlen_fwd_args(**over)) == fa2.FA2_OK
     assert lib.fa2_bwd_varlen(*varlen_bwd_args(**over)) == fa2.FA2_OK
+
+
+def sparse_args(fn, **over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, lse=FAKE, dout=FAKE, dq=FAKE, dk=FAKE, dv=FAKE, ws=FAKE,
+             ws_bytes=4096, B=1, H=2, N=300, d=64, scale=0.125, causal=1, wl=-1, wr=-1, alibi=None, mask=FAKE,
+             sb=0, sh=9, stream=None)
+    a.update(over)
+    if fn == "fa2_fwd_blocksparse":
+        keys = ("q", "k", "v", "out", "lse", "B", "H", "N", "d", "scale", "causal", "wl", "wr", "alibi", "mask", "sb",
+                "sh", "stream")
+    else:
+        keys = ("q", "k", "v", "out", "lse", "dout", "dq", "dk", "dv", "ws", "ws_bytes", "B", "H", "N", "d", "scale",
+                "causal", "wl", "wr", "alibi", "mask", "sb", "sh", "stream")
+    return [a[k] for k in keys]
+
+
+BAD_SPARSE = [
+    (dict(mask=None), fa2.FA2_ERR_INVALID_ARG),
+    (dict(sb=-1), fa2.FA2_ERR_INVALID_ARG),
+    (dict(sh=-9), fa2.FA2_ERR_INVALID_ARG),
+    (dict(N=65537), fa2.FA2_ERR_UNSUPPORTED),
+    (dict(d=80), fa2.FA2_ERR_UNSUPPORTED),
+    (dict(N=-2), fa2.FA2_ERR_INVALID_ARG),
+    (dict(scale=math.nan), fa2.FA2_ERR_INVALID_ARG),
+    (dict(q=None), fa2.FA2_ERR_INVALID_ARG),
+    (dict(out=MISALIGNED), fa2.FA2_ERR_INVALID_ARG),
+]
+
+
+@pytest.mark.parametrize("fn", ["fa2_fwd_blocksparse", "fa2_bwd_blocksparse"])
+@pytest.mark.parametrize("over,status", BAD_SPARSE)
+def test_blocksparse_entry_points_reject_bad_arguments(lib, fn, over, status):
+    assert getattr(lib, fn)(*sparse_args(fn, **over)) == status
+
+
+@pytest.mark.parametrize("fn", ["fa2_fwd_blocksparse", "fa2_bwd_blocksparse"])
+def test_blocksparse_empty_problem_is_ok(lib, fn):
+    assert getattr(lib, fn)(*sparse_args(fn, B=0, mask=None)) == fa2.FA2_OK
+
+
+def test_blocksparse_backward_checks_workspace(lib):
+    args = sparse_args("fa2_bwd_blocksparse", ws_bytes=2 * 300 * 4 - 1)
+    assert lib.fa2_bwd_blocksparse(*args) == fa2.FA2_ERR_INVALID_ARG
 
 
 def test_workspace_size(lib):

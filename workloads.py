@@ -195,3 +195,48 @@ def sample_varlen_rows(total, H, count=256, seed=0):
     count = min(count, total * H)
     flat = np.sort(rng.choice(total * H, size=count, replace=False))
     return np.stack([flat // total, flat % total], axis=1).astype(np.int64)
+
+
+# Block-sparse workload: the causal N=8192 shape with a 128 x 128 block mask.
+@dataclasses.dataclass(frozen=True)
+class BlockSparseWorkload:
+    number: int
+    name: str
+    B: int
+    H: int
+    N: int
+    d: int
+    causal: bool
+    local: int          # key blocks r - local .. r are on (a band around the diagonal)
+    global_blocks: int  # the first key blocks are on for every query block
+    density: float      # every other block is on with this probability (seeded, per head)
+    dtype: str = "bf16"
+    window: tuple = (-1, -1)
+    alibi: bool = False
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+    def describe(self) -> str:
+        return (f"{self.name}: bf16 B={self.B} H={self.H} N={self.N} d={self.d} causal={int(self.causal)} "
+                f"mask: band {self.local}, {self.global_blocks} global, random {self.density}")
+
+
+SPARSE_WORKLOADS = {
+    7: BlockSparseWorkload(7, "bf16_blocksparse_causal_n8192_d128", 4, 32, 8192, 128, True, 1, 1, 0.1),
+}
+
+
+def sparse_block_mask(H, N, local=1, global_blocks=1, density=0.1, seed=0, block=128) -> torch.Tensor:
+    """uint8 [1, H, nb, nb] block mask shared by every batch entry: for query block r,
+    key blocks r - local .. r + local, the first `global_blocks` ones and a seeded
+    random `density` share of the rest are on."""
+    nb = -(-N // block)
+    rng = np.random.default_rng(seed)
+    m = (rng.random((H, nb, nb)) < density)
+    r = np.arange(nb)[:, None]
+    c = np.arange(nb)[None, :]
+    m |= (np.abs(r - c) <= local)[None]
+    m[:, :, :global_blocks] = True
+    return torch.from_numpy(m.astype(np.uint8))[None]

@@ -10,9 +10,14 @@ line.
 After the timed steps, the packed variable-length workload (32768 tokens in 12
 ragged sequences, H=32, d=128, causal) is timed the same way through
 fa2_fwd_varlen / fa2_bwd_varlen and reported under "varlen", with the FLOP
-convention applied per sequence.
+convention applied per sequence. Then the block-sparse workload (the same
+B=4, H=32, N=8192, d=128 causal shape with a 128 x 128 block mask: a band of
+width 1 around the diagonal, one global key block and 10 % random blocks,
+about 18 % of the causal blocks) is timed through fa2_fwd_blocksparse /
+fa2_bwd_blocksparse and reported under "blocksparse", counting the visible
+(query, key) pairs of the active blocks.
 
-  python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-varlen]
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-varlen] [--no-sparse]
 """
 from __future__ import annotations
 
@@ -132,6 +137,74 @@ def bench_varlen(fa2, workloads, steps, warmup):
     }
 
 
+def causal_block_pairs(N, block=128):
+    """[nb, nb] number of causal-visible (query, key) pairs in each block pair."""
+    import numpy as np
+    nb = -(-N // block)
+    out = np.zeros((nb, nb))
+    for r in range(nb):
+        i = np.arange(r * block, min(N, r * block + block))
+        for c in range(r + 1):
+            s, e = c * block, min(N, c * block + block)
+            out[r, c] = np.clip(i - s + 1, 0, e - s).sum()
+    return out
+
+
+def bench_blocksparse(fa2, workloads, steps, warmup):
+    """Block-sparse workload: fa2_fwd_blocksparse + fa2_bwd_blocksparse, timed with events.
+    FLOPs: 4*d per visible pair of the active blocks (forward), 2.5x that (backward)."""
+    import torch
+    w = workloads.SPARSE_WORKLOADS[7]
+    B, H, N, d = w.B, w.H, w.N, w.d
+    t = workloads.make_inputs(B, H, N, d, "bf16", seed=w.number, with_dout=True)
+    mask = workloads.sparse_block_mask(H, N, w.local, w.global_blocks, w.density, seed=w.number)
+    q, k, v, do = (t[n].cuda() for n in ("q", "k", "v", "dout"))
+    del t
+    m = mask.cuda()
+    nb = m.shape[-1]
+    sh = nb * nb  # [1, H, nb, nb]: shared across the batch
+    out = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws_bytes = fa2.fa2_bwd_workspace_size(B, H, N, d)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+
+    def fwd():
+        fa2.fa2_fwd_blocksparse(q, k, v, out, lse, B, H, N, d, w.scale, 1, -1, -1, None, m, 0, sh, sp)
+
+    def bwd():
+        fa2.fa2_bwd_blocksparse(q, k, v, out, lse, do, dq, dk, dv, ws, ws_bytes, B, H, N, d, w.scale, 1, -1, -1, None,
+                                m, 0, sh, sp)
+
+    ms = timed([("fwd", fwd), ("bwd", bwd)], steps, warmup, stream)
+    per_block = causal_block_pairs(N)
+    active = mask[0].numpy().astype(bool)
+    pairs = B * float((per_block[None] * active).sum())
+    dense_pairs = B * H * float(per_block.sum())
+    f_fwd = 4.0 * d * pairs
+    f_bwd = 2.5 * f_fwd
+    fwd_tf = f_fwd / (ms["fwd"] * 1e-3) / 1e12
+    bwd_tf = f_bwd / (ms["bwd"] * 1e-3) / 1e12
+    step_ms = ms["fwd"] + ms["bwd"]
+    step_tf = (f_fwd + f_bwd) / (step_ms * 1e-3) / 1e12
+    return {
+        "workload": (f"bf16 block-sparse causal attention fwd+bwd, B={B} H={H} N={N} d={d}, 128x128 block mask: "
+                     f"band {w.local}, {w.global_blocks} global block, {w.density:.0%} random (seeded per head)"),
+        "active_pair_fraction": round(pairs / dense_pairs, 4),
+        "fwd_ms": round(ms["fwd"], 4),
+        "bwd_ms": round(ms["bwd"], 4),
+        "step_ms": round(step_ms, 4),
+        "fwd_tflops": round(fwd_tf, 2),
+        "bwd_tflops": round(bwd_tf, 2),
+        "tflops": round(step_tf, 2),
+        "frac_of_peak": round(step_tf / PEAK_BF16_TFLOPS, 4),
+        "fwd_frac_of_peak": round(fwd_tf / PEAK_BF16_TFLOPS, 4),
+        "flop_convention": "4*d per visible (query, key) pair of the active blocks forward, backward 2.5x",
+    }
+
+
 def recorded_traffic(call):
     """HBM bytes per launch of the dominant kernel from the committed rocprofv3
     FETCH_SIZE / WRITE_SIZE passes (profiles/hbm_traffic.json), reported only if
@@ -161,6 +234,9 @@ def main():
     ap.add_argument("--no-varlen", action="store_true", help="skip the packed variable-length measurement")
     ap.add_argument("--varlen-only", action="store_true",
                     help="only time the packed variable-length workload (prints its object as the JSON line)")
+    ap.add_argument("--no-sparse", action="store_true", help="skip the block-sparse measurement")
+    ap.add_argument("--sparse-only", action="store_true",
+                    help="only time the block-sparse workload (prints its object as the JSON line)")
     ap.add_argument("--atomic-dq", action="store_true",
                     help="time the float-atomic dQ variant of the backward instead of the default passes")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -190,6 +266,9 @@ def main():
     fa2.load_library()
     if args.varlen_only:
         print(json.dumps({"varlen": bench_varlen(fa2, workloads, args.steps, args.warmup)}), flush=True)
+        return
+    if args.sparse_only:
+        print(json.dumps({"blocksparse": bench_blocksparse(fa2, workloads, args.steps, args.warmup)}), flush=True)
         return
     w = workloads.WORKLOADS[3]  # B=4, H=32, N=8192, d=128, causal
     B, H, N, d = w.B, w.H, w.N, w.d
@@ -305,6 +384,9 @@ def main():
     }
     if not args.no_varlen:
         rec["varlen"] = bench_varlen(fa2, workloads, args.steps, args.warmup)
+    if not args.no_sparse:
+        rec["blocksparse"] = bench_blocksparse(fa2, workloads, args.steps, args.warmup)
+        rec["blocksparse"]["speedup_vs_dense_step"] = round(ms_step / rec["blocksparse"]["step_ms"], 3)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(rec), flush=True)

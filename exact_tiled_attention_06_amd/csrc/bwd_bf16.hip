@@ -184,6 +184,7 @@ __global__ __launch_bounds__(NW * 64, ((D == 128 && !DET) ? 4 : 8) / NW) void bw
 #pragma unroll
   for (int ks = 0; ks < S::KS; ++ks)
     vf[ks] = kj < N ? *reinterpret_cast<const bf16x8*>(vg + (int64_t)kj * rs + 16 * ks + 8 * hh) : bf16x8{};
+  wait_vm_all();
   // Resident K tile (B operand of S, and K of dQ = dS K).
   dma_tile<D, S::BK, NW>(k_lds, kg, rs, k0, N, w, lane);
 
@@ -265,9 +266,8 @@ __global__ __launch_bounds__(NW * 64, ((D == 128 && !DET) ? 4 : 8) / NW) void bw
 #pragma unroll
       for (int n = 0; n < PER_WAVE; ++n) {
         char* dst = st + (w * PER_WAVE + n) * 1024;
-        __builtin_amdgcn_global_load_lds((const void FA2_GLOBAL*)(qgb + dma_off[n]), (void FA2_LDS*)dst, 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((const void FA2_GLOBAL*)(ogb + dma_off[n]),
-                                         (void FA2_LDS*)(dst + S::QT_BYTES), 16, 0, 0);
+        dma16(qgb, dma_off[n], dst);
+        dma16(ogb, dma_off[n], dst + S::QT_BYTES);
       }
     } else {  // last, partial block: clamp rows to the sequence
       dma_tile<D, S::BQ, S::NW>(st, qg, rs, i0, N, w, lane);
@@ -276,17 +276,17 @@ __global__ __launch_bounds__(NW * 64, ((D == 128 && !DET) ? 4 : 8) / NW) void bw
     if (w == 0) {
       const int q = min(i0 + l32, N - 1);
       const float* src = hh ? del_g + q : lse_g + q;
-      __builtin_amdgcn_global_load_lds((const void FA2_GLOBAL*)src, (void FA2_LDS*)(st + 2 * S::QT_BYTES), 4, 0, 0);
+      dma4(src, st + 2 * S::QT_BYTES);
     }
   };
 
-  // Query block it + 1 must have landed; NST - 2 younger blocks may still be in
-  // flight (wave 0 issues one extra load per block, for LSE and D).
-  auto wait_next = [&]() __attribute__((always_inline)) {
+  // Waits until the next query block has landed; `younger` blocks issued after
+  // it may stay in flight (wave 0 issues one extra load per block, for LSE and D).
+  auto wait_next = [&](int younger) __attribute__((always_inline)) {
     if (w == 0) {
-      wait_vm_and_sync<(2 * PER_WAVE + 1) * (NST - 2)>();
+      wait_ring<NST, 2 * PER_WAVE + 1>(younger);
     } else {
-      wait_vm_and_sync<2 * PER_WAVE * (NST - 2)>();
+      wait_ring<NST, 2 * PER_WAVE>(younger);
     }
   };
 
@@ -416,14 +416,14 @@ __global__ __launch_bounds__(NW * 64, ((D == 128 && !DET) ? 4 : 8) / NW) void bw
         if (i0 + m < N) atomicAdd(dq_row + (int64_t)m * D, dqa[r]);
       }
     }
-    wait_next();
+    wait_next(n_tiles - u - 2);  // block u + 1
   };
 
   static_for<0, NST - 1>([&](auto sc) {
     constexpr int k = decltype(sc)::value;
     if (k < n_tiles) issue_q((int)(entry_at(k) & kTileIndexMask), std::integral_constant<int, k>{});
   });
-  wait_next();
+  wait_next(n_tiles - 1);  // block 0
   for (int u = 0; u < n_tiles; u += NST) {
     static_for<0, NST>([&](auto sc) {
       constexpr int k = decltype(sc)::value;
@@ -553,9 +553,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq_det_kernel(BwdParams p
 #pragma unroll
       for (int n = 0; n < PER_WAVE; ++n) {
         char* dst = kl + (w * PER_WAVE + n) * 1024;
-        __builtin_amdgcn_global_load_lds((const void FA2_GLOBAL*)(kgb + dma_off[n]), (void FA2_LDS*)dst, 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((const void FA2_GLOBAL*)(vgb + dma_off[n]), (void FA2_LDS*)(dst + TILE), 16,
-                                         0, 0);
+        dma16(kgb, dma_off[n], dst);
+        dma16(vgb, dma_off[n], dst + TILE);
       }
     } else {
       dma_tile<D, BC, NW>(kl, kg, rs, row0, N, w, lane);
@@ -622,14 +621,15 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq_det_kernel(BwdParams p
         }
       }
     }
-    wait_vm_and_sync<2 * PER_WAVE * (NST - 2)>();  // tile t + 1 has landed
+    wait_ring<NST, 2 * PER_WAVE>(n_tiles - u - 2);  // tile u + 1 has landed
   };
 
+  wait_vm_all();
   static_for<0, NST - 1>([&](auto sc) {
     constexpr int k = decltype(sc)::value;
     if (k < n_tiles) issue(tile_at(k), std::integral_constant<int, k>{});
   });
-  wait_vm_and_sync<2 * PER_WAVE * (NST - 2)>();
+  wait_ring<NST, 2 * PER_WAVE>(n_tiles - 1);  // tile 0 has landed
   for (int u = 0; u < n_tiles; u += NST) {
     static_for<0, NST>([&](auto sc) {
       constexpr int k = decltype(sc)::value;

@@ -113,19 +113,41 @@ __device__ __forceinline__ uint32_t tile_off_tr(int r, int col) {
   return tile_off<D>(r, col >> 3) + (col & 7) * 2;
 }
 
+// Direct global->LDS loads (gfx950 global_load_lds_dword / _dwordx4): lane i
+// of the wave reads its own global address and the data lands in LDS at
+// lds_dst + 4*i (dword) or + 16*i (dwordx4); no register receives it. They are
+// issued from inline assembly on purpose: the compiler treats its own builtin
+// for these loads as an LDS store of unknown extent and fences every later
+// transposed LDS read (ds_read_b64_tr_b16) with s_waitcnt vmcnt(0), which
+// drains the whole prefetch ring at each tile. Here the kernels track
+// completion themselves (wait_vm_and_sync with the ring's exact count; vector
+// loads complete in issue order). The asm has no outputs: nothing is written
+// to a register while the load is in flight. M0 (the LDS destination) is an
+// input the compiler sets; s_nop 0 separates that write from the load.
+//   dma16: base (uniform) + voff (per lane, bytes); dma4: a per-lane address.
+__device__ __forceinline__ void dma16(const void* base, uint32_t voff, const char* lds_dst) {
+  const uint32_t m0 = (uint32_t)(uintptr_t)(const void FA2_LDS*)lds_dst;
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "{m0}"(m0) : "memory");
+}
+__device__ __forceinline__ void dma4(const void* addr, const char* lds_dst) {
+  const uint32_t m0 = (uint32_t)(uintptr_t)(const void FA2_LDS*)lds_dst;
+  asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(addr), "{m0}"(m0) : "memory");
+}
+
 // Copies rows [row0, row0 + ROWS) of one head (row stride rs elements) into
-// an LDS tile laid out with tile_off, using gfx950's direct global->LDS loads
-// (global_load_lds_dwordx4: lane i of a wave writes LDS bytes base + 16*i).
-// Each lane loads the 16-byte chunk that the swizzle places at its LDS slot.
-// Rows at or past n_rows read row n_rows - 1 (finite data that the caller
-// masks), so no load leaves the tensor. The caller waits (s_waitcnt) and
-// synchronises before reading the tile.
+// an LDS tile laid out with tile_off, using the direct global->LDS loads
+// (PER_WAVE dwordx4 loads per wave). Each lane loads the 16-byte chunk that
+// the swizzle places at its LDS slot. Rows at or past n_rows read row
+// n_rows - 1 (finite data that the caller masks), so no load leaves the
+// tensor; row0 < n_rows. The caller waits (s_waitcnt) and synchronises before
+// reading the tile.
 template <int D, int ROWS, int NW>
 __device__ __forceinline__ void dma_tile(char* lds_tile, const bf16* g, int64_t rs, int row0, int n_rows,
                                          int w, int lane) {
   constexpr int BYTES = ROWS * D * 2;
   constexpr int PER_WAVE = BYTES / (1024 * NW);
   static_assert(BYTES % (1024 * NW) == 0, "tile must split into 1 KB pieces per wave");
+  const bf16* tile_base = g + (int64_t)row0 * rs;
 #pragma unroll
   for (int n = 0; n < PER_WAVE; ++n) {
     const int m = w * PER_WAVE + n;
@@ -134,8 +156,7 @@ __device__ __forceinline__ void dma_tile(char* lds_tile, const bf16* g, int64_t 
     const int slot = (byte % (2 * D)) >> 4;
     const int cc = slot ^ tile_swz<D>(r);
     const int row = min(row0 + r, n_rows - 1);
-    const bf16* src = g + (int64_t)row * rs + cc * 8;
-    __builtin_amdgcn_global_load_lds((const void FA2_GLOBAL*)src, (void FA2_LDS*)(lds_tile + m * 1024), 16, 0, 0);
+    dma16(tile_base, (uint32_t)(((row - row0) * rs + cc * 8) * 2), lds_tile + m * 1024);
   }
 }
 
@@ -144,6 +165,15 @@ __device__ __forceinline__ void dma_tile(char* lds_tile, const bf16* g, int64_t 
 __device__ __forceinline__ void wait_all_and_sync() {
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+}
+
+// Wait for every outstanding vector-memory load of this wave. Called once,
+// after the per-lane register loads of a kernel's prologue and before its
+// prefetch ring starts: the compiler then knows that no register load is
+// pending inside the tile loop and adds no vmcnt wait of its own there (such a
+// wait would also drain the ring's direct loads in flight).
+__device__ __forceinline__ void wait_vm_all() {
+  __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0); expcnt, lgkmcnt: no wait
 }
 
 // Wait until at most N vector-memory operations of this wave are outstanding
@@ -155,6 +185,25 @@ __device__ __forceinline__ void wait_vm_and_sync() {
   // s_waitcnt: vmcnt[3:0] | expcnt[6:4] (7 = no wait) | lgkmcnt[11:8] | vmcnt[5:4] at [15:14]
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | ((N >> 4) << 14));
   __syncthreads();
+}
+
+// Prefetch ring of NST stages, PER direct loads per tile per wave: waits until
+// the next tile to compute has landed and synchronises the workgroup.
+// `younger` = the number of tiles issued after that one (tile loads complete
+// in issue order, so those may stay in flight); it is at most NST - 2 and
+// drops to zero or below at the end of the ring, where the wait must cover
+// everything.
+template <int NST, int PER>
+__device__ __forceinline__ void wait_ring(int younger) {
+  if constexpr (NST <= 2) {
+    wait_vm_and_sync<0>();
+  } else {
+    if (younger >= NST - 2) {
+      wait_vm_and_sync<PER * (NST - 2)>();
+    } else {
+      wait_ring<NST - 1, PER>(younger);
+    }
+  }
 }
 
 template <int I, int N, typename F>

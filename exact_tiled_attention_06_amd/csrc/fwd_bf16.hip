@@ -72,8 +72,12 @@ struct FwdShape {
   static constexpr int ROWB = 2 * D;        // bytes per LDS row
 };
 
+// Occupancy hint: with d = 128 the LDS ring (64 KB per workgroup) caps a CU at
+// 2 waves per SIMD. Stating it lets the scheduler use the registers to hide
+// LDS latency instead of saving them for occupancy it cannot reach.
 template <int D, int NW, int BC, int NST, bool ALIBI, bool VARLEN, bool SPARSE>
-__global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(FwdParams p) {
+__global__ __launch_bounds__(NW * 64, 8 / NW)
+__attribute__((amdgpu_waves_per_eu(D == 128 ? 2 : 1, D == 128 ? 2 : 8))) void fwd_bf16_kernel(FwdParams p) {
   using S = FwdShape<D, NW, BC, NST>;
   static_assert(!(VARLEN && SPARSE), "packed batches have no block mask");
   static_assert(!SPARSE || S::BR == kSparseBlock, "a workgroup covers one mask row");
@@ -184,9 +188,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(FwdParams p) 
 #pragma unroll
       for (int n = 0; n < PER_WAVE; ++n) {
         char* dst = kl + (w * PER_WAVE + n) * 1024;
-        __builtin_amdgcn_global_load_lds((const void FA2_GLOBAL*)(kgb + dma_off[n]), (void FA2_LDS*)dst, 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((const void FA2_GLOBAL*)(vgb + dma_off[n]), (void FA2_LDS*)(dst + S::TILE),
-                                         16, 0, 0);
+        dma16(kgb, dma_off[n], dst);
+        dma16(vgb, dma_off[n], dst + S::TILE);
       }
     } else {  // last, partial tile: clamp rows to the sequence
       dma_tile<D, BC, NW>(kl, kg, rs, row0, N, w, lane);
@@ -210,19 +213,31 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(FwdParams p) 
       const char* kb = smem + st * S::STAGE;
       const char* vb = kb + S::TILE;
 
-      // S^T = K Q^T for each 32-key subtile.
+      // S^T = K Q^T for each 32-key subtile. The K fragments of reduction step
+      // ks + 1 are read while the MFMAs of step ks run (two register buffers).
       f32x16 s[S::NSUB];
 #pragma unroll
       for (int sub = 0; sub < S::NSUB; ++sub) s[sub] = f32x16{};
+      bf16x8 ka[2][S::NSUB];
+      auto kload = [&](int ks, bf16x8(&dst)[S::NSUB]) __attribute__((always_inline)) {
 #pragma unroll
-      for (int ks = 0; ks < S::KS; ++ks) {
-        const uint32_t ka = kbase ^ (ks << 5);
+        for (int sub = 0; sub < S::NSUB; ++sub) dst[sub] = lds_read16(kb + sub * 32 * S::ROWB, kbase ^ (ks << 5));
+      };
+      kload(0, ka[0]);
+      static_for<0, S::KS>([&](auto kc) {
+        constexpr int ks = decltype(kc)::value;
+        if constexpr (ks + 1 < S::KS) kload(ks + 1, ka[(ks + 1) & 1]);
 #pragma unroll
-        for (int sub = 0; sub < S::NSUB; ++sub) {
-          const bf16x8 a = lds_read16(kb + sub * 32 * S::ROWB, ka);
-          s[sub] = mfma32(a, qf[ks], s[sub]);
-        }
-      }
+        for (int sub = 0; sub < S::NSUB; ++sub) s[sub] = mfma32(ka[ks & 1][sub], qf[ks], s[sub]);
+      });
+      // Keep that order in the schedule: the reads of steps 0 and 1, then per
+      // step its MFMAs followed by the reads of the step after next.
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * S::NSUB, 0);  // LDS reads
+      static_for<0, S::KS>([&](auto kc) {
+        constexpr int ks = decltype(kc)::value;
+        __builtin_amdgcn_sched_group_barrier(0x100, ks + 1 < S::KS ? S::NSUB : 0, 0);  // LDS reads
+        __builtin_amdgcn_sched_group_barrier(0x008, S::NSUB, 0);                       // MFMAs
+      });
 
       // Bias (ALiBi, in log2 units) and masks; masks only on tiles crossing an edge.
       if (ALIBI) {
@@ -273,38 +288,46 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(FwdParams p) 
         vx_lo[mb] = vbase_lo ^ (mb << 6);
         vx_hi[mb] = vbase_hi ^ (mb << 6);
       }
+      // One step per 16 keys (subtile sub = step / 2, half kk = step % 2); the V^T
+      // fragments of step + 1 are read while the MFMAs of step run.
+      bf16x8 va[2][S::MB];
+      auto vload = [&](int step, bf16x8(&dst)[S::MB]) __attribute__((always_inline)) {
+        const int rowoff = step * 16 * S::ROWB;
 #pragma unroll
-      for (int sub = 0; sub < S::NSUB; ++sub) {
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          float pv[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float x = s[sub][8 * kk + e];
-            pv[e] = ALIBI ? fast_exp2(x - m2) : fast_exp2(fmaf(x, p.scale_log2, -m2));
-          }
-          const bf16x8 pb = pack_bf16x8(pv[0], pv[1], pv[2], pv[3], pv[4], pv[5], pv[6], pv[7]);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) lsum[e & 3] += pv[e];
-          const int rowoff = (2 * sub + kk) * 16 * S::ROWB;
-#pragma unroll
-          for (int mb = 0; mb < S::MB; ++mb) {
-            const bf16x4 lo = lds_read_tr(vb + rowoff + vx_lo[mb]);
-            const bf16x4 hi = lds_read_tr(vb + rowoff + vx_hi[mb]);
-            o[mb] = mfma32(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), pb, o[mb]);
-          }
+        for (int mb = 0; mb < S::MB; ++mb) {
+          const bf16x4 lo = lds_read_tr(vb + rowoff + vx_lo[mb]);
+          const bf16x4 hi = lds_read_tr(vb + rowoff + vx_hi[mb]);
+          dst[mb] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         }
-      }
+      };
+      vload(0, va[0]);
+      static_for<0, 2 * S::NSUB>([&](auto sc) {
+        constexpr int step = decltype(sc)::value;
+        constexpr int sub = step / 2, kk = step % 2;
+        if constexpr (step + 1 < 2 * S::NSUB) vload(step + 1, va[(step + 1) & 1]);
+        float pv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float x = s[sub][8 * kk + e];
+          pv[e] = ALIBI ? fast_exp2(x - m2) : fast_exp2(fmaf(x, p.scale_log2, -m2));
+        }
+        const bf16x8 pb = pack_bf16x8(pv[0], pv[1], pv[2], pv[3], pv[4], pv[5], pv[6], pv[7]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) lsum[e & 3] += pv[e];
+#pragma unroll
+        for (int mb = 0; mb < S::MB; ++mb) o[mb] = mfma32(va[step & 1][mb], pb, o[mb]);
+      });
     }
-    // Tile t + 1 must have landed; the NST - 2 younger tiles may still be in flight.
-    wait_vm_and_sync<S::VM_PER_TILE * (NST - 2)>();
+    // Tile u + 1 must have landed; the tiles issued after it may still be in flight.
+    wait_ring<NST, S::VM_PER_TILE>(n_tiles - u - 2);
   };
 
+  wait_vm_all();
   static_for<0, NST - 1>([&](auto sc) {
     constexpr int k = decltype(sc)::value;
     if (k < n_tiles) issue(tile_at(k), std::integral_constant<int, k>{});
   });
-  wait_vm_and_sync<S::VM_PER_TILE * (NST - 2)>();
+  wait_ring<NST, S::VM_PER_TILE>(n_tiles - 1);  // tile 0 has landed
   for (int u = 0; u < n_tiles; u += NST) {
     static_for<0, NST>([&](auto sc) {
       constexpr int k = decltype(sc)::value;

@@ -575,12 +575,44 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq_det_kernel(BwdParams p
       const char* kb = smem + st * STAGE;
       const char* vb = kb + TILE;
       // S^T = K Q^T and dP^T = V dO^T: rows are keys (A lane m reads row kperm(m)), columns queries.
+      // The K and V fragments of step ks + 1 are read while the MFMAs of step ks run.
       f32x16 s = f32x16{}, dp = f32x16{};
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
+      bf16x8 kv[2][2];
+      auto kvload = [&](int ks, bf16x8(&dst)[2]) __attribute__((always_inline)) {
         const uint32_t ax = abase ^ (ks << 5);
-        s = mfma32(lds_read16(kb, ax), qf[ks], s);
-        dp = mfma32(lds_read16(vb, ax), of[ks], dp);
+        dst[0] = lds_read16(kb, ax);
+        dst[1] = lds_read16(vb, ax);
+      };
+      kvload(0, kv[0]);
+      static_for<0, KS>([&](auto kc) {
+        constexpr int ks = decltype(kc)::value;
+        if constexpr (ks + 1 < KS) kvload(ks + 1, kv[(ks + 1) & 1]);
+        s = mfma32(kv[ks & 1][0], qf[ks], s);
+        dp = mfma32(kv[ks & 1][1], of[ks], dp);
+      });
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // LDS reads of steps 0 and 1
+      static_for<0, KS>([&](auto kc) {
+        constexpr int ks = decltype(kc)::value;
+        __builtin_amdgcn_sched_group_barrier(0x100, ks + 1 < KS ? 2 : 0, 0);  // reads of step ks + 2
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                    // MFMAs of step ks
+      });
+      // K^T fragments for dQ^T += K^T dS^T (both 16-key halves), read ahead of the softmax.
+      uint32_t tx_lo[MB], tx_hi[MB];
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        tx_lo[mb] = tr_lo ^ (mb << 6);
+        tx_hi[mb] = tr_hi ^ (mb << 6);
+      }
+      bf16x8 kt[2][MB];
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const int ro = kk * 16 * ROWB;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          const bf16x4 lo = lds_read_tr(kb + ro + tx_lo[mb]);
+          const bf16x4 hi = lds_read_tr(kb + ro + tx_hi[mb]);
+          kt[kk][mb] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        }
       }
       float pr[16];
 #pragma unroll
@@ -599,26 +631,15 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq_det_kernel(BwdParams p
           pr[r] = vis ? pr[r] : 0.f;
         }
       }
-      uint32_t tx_lo[MB], tx_hi[MB];
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        tx_lo[mb] = tr_lo ^ (mb << 6);
-        tx_hi[mb] = tr_hi ^ (mb << 6);
-      }
-      // dQ^T += K^T dS^T: A = K^T read transposed from the K tile, B = dS^T from registers.
+      // dQ^T += K^T dS^T: A = K^T (read above), B = dS^T from registers.
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
         float d8[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) d8[e] = pr[8 * kk + e] * (dp[8 * kk + e] - delta);
         const bf16x8 dsb = pack_bf16x8(d8[0], d8[1], d8[2], d8[3], d8[4], d8[5], d8[6], d8[7]);
-        const int ro = kk * 16 * ROWB;
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-          const bf16x4 lo = lds_read_tr(kb + ro + tx_lo[mb]);
-          const bf16x4 hi = lds_read_tr(kb + ro + tx_hi[mb]);
-          acc[mb] = mfma32(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), dsb, acc[mb]);
-        }
+        for (int mb = 0; mb < MB; ++mb) acc[mb] = mfma32(kt[kk][mb], dsb, acc[mb]);
       }
     }
     wait_ring<NST, 2 * PER_WAVE>(n_tiles - u - 2);  // tile u + 1 has landed

@@ -72,12 +72,17 @@ struct FwdShape {
   static constexpr int ROWB = 2 * D;        // bytes per LDS row
 };
 
-// Occupancy hint: with d = 128 the LDS ring (64 KB per workgroup) caps a CU at
-// 2 waves per SIMD. Stating it lets the scheduler use the registers to hide
-// LDS latency instead of saving them for occupancy it cannot reach.
+// Occupancy hint: with d = 128 and 32-key tiles the LDS ring takes 32 KB per
+// workgroup, so three workgroups (3 waves per SIMD, 96 KB of LDS) share a CU.
+// Stating the figure lets the scheduler spend up to 168 registers per lane
+// instead of saving them for occupancy that would not help: three waves per SIMD
+// already keep the LDS port busy while one of them waits on its MFMAs.
+#ifndef FA2_FWD_OCC
+#define FA2_FWD_OCC 3
+#endif
 template <int D, int NW, int BC, int NST, bool ALIBI, bool VARLEN, bool SPARSE>
-__global__ __launch_bounds__(NW * 64, 8 / NW)
-__attribute__((amdgpu_waves_per_eu(D == 128 ? 2 : 1, D == 128 ? 2 : 8))) void fwd_bf16_kernel(FwdParams p) {
+__global__ __launch_bounds__(NW * 64, (D == 128 ? 4 * FA2_FWD_OCC : 8) / NW)
+__attribute__((amdgpu_waves_per_eu(D == 128 ? FA2_FWD_OCC : 1, D == 128 ? FA2_FWD_OCC : 8))) void fwd_bf16_kernel(FwdParams p) {
   using S = FwdShape<D, NW, BC, NST>;
   static_assert(!(VARLEN && SPARSE), "packed batches have no block mask");
   static_assert(!SPARSE || S::BR == kSparseBlock, "a workgroup covers one mask row");
@@ -382,11 +387,14 @@ static hipError_t launch_fwd_cfg(const FwdParams& p0, hipStream_t stream) {
 #define FA2_FWD_NST 2
 #endif
 
+#ifndef FA2_FWD_BC
+#define FA2_FWD_BC 32
+#endif
 template <int D, bool VARLEN, bool SPARSE>
 static hipError_t launch_fwd_d(const FwdParams& p, hipStream_t stream) {
-  constexpr int NW = FA2_FWD_NW, NST = FA2_FWD_NST;
-  return p.alibi != nullptr ? launch_fwd_cfg<D, NW, 64, NST, true, VARLEN, SPARSE>(p, stream)
-                            : launch_fwd_cfg<D, NW, 64, NST, false, VARLEN, SPARSE>(p, stream);
+  constexpr int NW = FA2_FWD_NW, NST = FA2_FWD_NST, BC = D == 128 ? FA2_FWD_BC : 64;
+  return p.alibi != nullptr ? launch_fwd_cfg<D, NW, BC, NST, true, VARLEN, SPARSE>(p, stream)
+                            : launch_fwd_cfg<D, NW, BC, NST, false, VARLEN, SPARSE>(p, stream);
 }
 
 template <int D>

@@ -392,7 +392,7 @@ static hipError_t launch_fwd_cfg(const FwdParams& p0, hipStream_t stream) {
 #endif
 template <int D, bool VARLEN, bool SPARSE>
 static hipError_t launch_fwd_d(const FwdParams& p, hipStream_t stream) {
-  constexpr int NW = FA2_FWD_NW, NST = FA2_FWD_NST, BC = D == 128 ? FA2_FWD_BC : 64;
+  constexpr int NW = SPARSE ? kSparseBlock / 32 : FA2_FWD_NW, NST = FA2_FWD_NST, BC = D == 128 ? FA2_FWD_BC : 64;
   return p.alibi != nullptr ? launch_fwd_cfg<D, NW, BC, NST, true, VARLEN, SPARSE>(p, stream)
                             : launch_fwd_cfg<D, NW, BC, NST, false, VARLEN, SPARSE>(p, stream);
 }

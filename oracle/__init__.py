@@ -27,3 +27,12 @@ from .blocksparse import (  # noqa: F401
     blocksparse_forward,
     blocksparse_forward_rows,
 )
+from .dropout import (  # noqa: F401
+    dropout_backward,
+    dropout_backward_sampled,
+    dropout_forward,
+    dropout_forward_rows,
+    keep_rows,
+    keep_threshold,
+    philox4x64,
+)

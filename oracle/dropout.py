@@ -1,0 +1,208 @@
+"""fp64 CPU oracle for attention with dropout on the attention weights — TEST INFRASTRUCTURE ONLY.
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg may import
+this module; the HIP library and its binding never do.
+
+Source: the wmrh.cn FlashAttention v2 article, section 5.1 (API), lists a
+`dropout_p` argument next to the ones the dense oracle covers; the page fixes no
+random-number generator and no formula. The plainest reading, stated here and in
+the design notes:
+
+  * Dropout acts on the normalised attention weights: with P = softmax(S) (the
+    dense definition, masks and ALiBi included) and a keep matrix Z of 0/1
+    entries, O = (P * Z) V / (1 - p). Each weight is kept with probability
+    1 - p and the survivors are scaled so that E[O] is the undropped output.
+  * The saved statistic is unchanged: LSE is that of the undropped softmax.
+  * Z comes from a counter-based generator, so the backward can regenerate it:
+    Philox4x64-10 (Salmon, Moraes, Dror and Shaw, "Parallel random numbers: as
+    easy as 1, 2, 3", SC 2011), with
+      key     = (seed, offset)                              two 64-bit words
+      counter = (j // 16, i, b * H + h, 0)                  four 64-bit words
+    The four 64-bit output words give sixteen 16-bit values; key j of the group
+    takes value t = j % 16, i.e. bits 16 * (t % 4) .. +15 of word t // 4.
+  * Keep iff that value < T, T = floor((1 - p) * 65536 + 0.5) computed in fp64
+    from the fp32 value of p (so p is resolved to 1/65536; p = 0 keeps all).
+  * Gradients by the chain rule: dV = (P * Z)^T dO / (1 - p);
+    dP = Z * (dO V^T) / (1 - p); D = rowsum(P * dP) = rowsum(dO * O);
+    dS = P * (dP - D); dQ = scale * dS K; dK = scale * dS^T Q.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from . import attention as oa
+
+# Philox4x64 round constants (the SC 2011 paper's multipliers and Weyl increments).
+PHILOX_M0 = 0xD2E7470EE14C6C93
+PHILOX_M1 = 0xCA5A826395121157
+PHILOX_W0 = 0x9E3779B97F4A7C15
+PHILOX_W1 = 0xBB67AE8584CAA73B
+ROUNDS = 10
+KEYS_PER_CALL = 16  # sixteen 16-bit values per call
+
+_M32 = np.uint64(0xFFFFFFFF)
+_S32 = np.uint64(32)
+
+
+def _mulhilo64(a, b):
+    """Full 128-bit product of uint64 arrays, from 32-bit halves: (hi, lo)."""
+    a0, a1 = a & _M32, a >> _S32
+    b0, b1 = b & _M32, b >> _S32
+    p00, p01, p10, p11 = a0 * b0, a0 * b1, a1 * b0, a1 * b1
+    mid = (p00 >> _S32) + (p01 & _M32) + (p10 & _M32)
+    lo = ((mid & _M32) << _S32) | (p00 & _M32)
+    hi = p11 + (p01 >> _S32) + (p10 >> _S32) + (mid >> _S32)
+    return hi, lo
+
+
+def philox4x64(counter, key, rounds=ROUNDS):
+    """Philox4x64-R on uint64 arrays. counter: [..., 4]; key: (k0, k1). Returns [..., 4]."""
+    c = [np.array(counter, dtype=np.uint64)[..., n].copy() for n in range(4)]
+    k0 = np.uint64(int(key[0]) & 0xFFFFFFFFFFFFFFFF)
+    k1 = np.uint64(int(key[1]) & 0xFFFFFFFFFFFFFFFF)
+    m0, m1 = np.uint64(PHILOX_M0), np.uint64(PHILOX_M1)
+    with np.errstate(over="ignore"):
+        for r in range(rounds):
+            if r:
+                k0 = np.uint64((int(k0) + PHILOX_W0) & 0xFFFFFFFFFFFFFFFF)
+                k1 = np.uint64((int(k1) + PHILOX_W1) & 0xFFFFFFFFFFFFFFFF)
+            hi0, lo0 = _mulhilo64(m0, c[0])
+            hi1, lo1 = _mulhilo64(m1, c[2])
+            c = [hi1 ^ c[1] ^ k0, lo1, hi0 ^ c[3] ^ k1, lo0]
+    return np.stack(c, axis=-1)
+
+
+def keep_threshold(dropout_p):
+    """T: a 16-bit value v keeps its weight iff v < T."""
+    p = float(np.float32(dropout_p))
+    if not 0.0 <= p < 1.0:
+        raise ValueError("dropout_p must be in [0, 1)")
+    return int(np.floor((1.0 - p) * 65536.0 + 0.5))
+
+
+def random_values(bh, rows, N, seed, offset):
+    """uint32 [len(rows), N]: the 16-bit value of every (query row, key) of head bh."""
+    rows = np.asarray(rows, dtype=np.uint64)
+    groups = np.arange((N + KEYS_PER_CALL - 1) // KEYS_PER_CALL, dtype=np.uint64)
+    ctr = np.zeros((len(rows), len(groups), 4), dtype=np.uint64)
+    ctr[..., 0] = groups[None, :]
+    ctr[..., 1] = rows[:, None]
+    ctr[..., 2] = np.uint64(bh)
+    words = philox4x64(ctr, (seed, offset))                       # [rows, groups, 4]
+    t = np.arange(KEYS_PER_CALL)
+    vals = (words[..., t // 4] >> (np.uint64(16) * (t % 4).astype(np.uint64))) & np.uint64(0xFFFF)
+    return vals.reshape(len(rows), -1)[:, :N].astype(np.uint32)
+
+
+def keep_rows(bh, rows, N, dropout_p, seed, offset):
+    """Boolean Z [len(rows), N] for head bh (= b * H + h)."""
+    return random_values(bh, rows, N, seed, offset) < keep_threshold(dropout_p)
+
+
+def _scale_of(dropout_p):
+    return 1.0 / (1.0 - float(np.float32(dropout_p)))
+
+
+def dropout_forward(q, k, v, dropout_p, seed, offset=0, softmax_scale=None, causal=False,
+                    window_size=(-1, -1), alibi_slopes=None):
+    """q, k, v: [B, N, H, d]. Returns (out [B, N, H, d], lse [B, H, N]); lse is undropped."""
+    q, k, v, scale, wl, wr, slopes = oa._prep(q, k, v, softmax_scale, window_size, alibi_slopes)
+    B, N, H, _ = q.shape
+    rp = _scale_of(dropout_p)
+    out = np.zeros((B, N, H, v.shape[-1]))
+    lse = np.zeros((B, H, N))
+    for b in range(B):
+        for h in range(H):
+            kh, vh = k[b, :, h, :], v[b, :, h, :]
+            for r0 in range(0, N, oa.ROW_CHUNK):
+                rows = np.arange(r0, min(N, r0 + oa.ROW_CHUNK))
+                s = oa.logits(q[b, rows, h, :], kh, rows, scale, causal, wl, wr, oa._slope(slopes, h))
+                p, lse_rows = oa.softmax_rows(s)
+                z = keep_rows(b * H + h, rows, N, dropout_p, seed, offset)
+                out[b, rows, h, :] = ((p * z) @ vh) * rp
+                lse[b, h, rows] = lse_rows
+    return out, lse
+
+
+def _dropout_row_grads(p, z, rp, do_rows, o_rows, vh):
+    """dP = Z * (dO V^T) / (1 - p), D = rowsum(dO * O), dS = P * (dP - D)."""
+    dp = (do_rows @ vh.T) * z * rp
+    dvec = np.sum(do_rows * o_rows, axis=1, keepdims=True)
+    return p * (dp - dvec)
+
+
+def dropout_backward(q, k, v, dout, dropout_p, seed, offset=0, softmax_scale=None, causal=False,
+                     window_size=(-1, -1), alibi_slopes=None):
+    """Gradients of sum(out * dout) with the same keep matrix as the forward. Returns (dq, dk, dv)."""
+    out, _ = dropout_forward(q, k, v, dropout_p, seed, offset, softmax_scale, causal, window_size, alibi_slopes)
+    q, k, v, scale, wl, wr, slopes = oa._prep(q, k, v, softmax_scale, window_size, alibi_slopes)
+    do = oa.to_f64(dout)
+    B, N, H, _ = q.shape
+    rp = _scale_of(dropout_p)
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    for b in range(B):
+        for h in range(H):
+            qh, kh, vh, doh = q[b, :, h, :], k[b, :, h, :], v[b, :, h, :], do[b, :, h, :]
+            for r0 in range(0, N, oa.ROW_CHUNK):
+                rows = np.arange(r0, min(N, r0 + oa.ROW_CHUNK))
+                s = oa.logits(qh[rows], kh, rows, scale, causal, wl, wr, oa._slope(slopes, h))
+                p, _ = oa.softmax_rows(s)
+                z = keep_rows(b * H + h, rows, N, dropout_p, seed, offset)
+                ds = _dropout_row_grads(p, z, rp, doh[rows], out[b, rows, h, :], vh)
+                dv[b, :, h, :] += ((p * z) * rp).T @ doh[rows]
+                dq[b, rows, h, :] = scale * (ds @ kh)
+                dk[b, :, h, :] += scale * (ds.T @ qh[rows])
+    return dq, dk, dv
+
+
+def dropout_forward_rows(q, k, v, rows_bhi, dropout_p, seed, offset=0, softmax_scale=None, causal=False,
+                         window_size=(-1, -1), alibi_slopes=None):
+    """The forward at sampled (b, h, i) rows. Returns (out [n, d], lse [n])."""
+    q, k, v, scale, wl, wr, slopes = oa._prep(q, k, v, softmax_scale, window_size, alibi_slopes)
+    B, N, H, _ = q.shape
+    rp = _scale_of(dropout_p)
+    rows_bhi = np.asarray(rows_bhi)
+    out = np.zeros((len(rows_bhi), v.shape[-1]))
+    lse = np.zeros(len(rows_bhi))
+    for n, (b, h, i) in enumerate(rows_bhi):
+        s = oa.logits(q[b, i, h, :][None, :], k[b, :, h, :], np.array([i]), scale, causal, wl, wr,
+                      oa._slope(slopes, h))
+        p, l = oa.softmax_rows(s)
+        z = keep_rows(b * H + h, [i], N, dropout_p, seed, offset)
+        out[n] = (((p * z) @ v[b, :, h, :]) * rp)[0]
+        lse[n] = l[0]
+    return out, lse
+
+
+def dropout_backward_sampled(q, k, v, dout, q_rows_bhi, k_rows_bhj, dropout_p, seed, offset=0,
+                             softmax_scale=None, causal=False, window_size=(-1, -1), alibi_slopes=None):
+    """The backward at sampled query rows (dQ) and key rows (dK, dV). Returns (dq_rows, dk_rows, dv_rows)."""
+    q, k, v, scale, wl, wr, slopes = oa._prep(q, k, v, softmax_scale, window_size, alibi_slopes)
+    do = oa.to_f64(dout)
+    B, N, H, _ = q.shape
+    rp = _scale_of(dropout_p)
+    q_rows_bhi, k_rows_bhj = np.asarray(q_rows_bhi), np.asarray(k_rows_bhj)
+
+    def head_rows(b, h, rows):
+        qh, kh, vh, doh = q[b, :, h, :], k[b, :, h, :], v[b, :, h, :], do[b, :, h, :]
+        s = oa.logits(qh[rows], kh, rows, scale, causal, wl, wr, oa._slope(slopes, h))
+        p, _ = oa.softmax_rows(s)
+        z = keep_rows(b * H + h, rows, N, dropout_p, seed, offset)
+        o_rows = ((p * z) @ vh) * rp
+        return p, z, _dropout_row_grads(p, z, rp, doh[rows], o_rows, vh)
+
+    dq_rows = np.zeros((len(q_rows_bhi), q.shape[-1]))
+    for n, (b, h, i) in enumerate(q_rows_bhi):
+        _, _, ds = head_rows(b, h, np.array([i]))
+        dq_rows[n] = scale * (ds @ k[b, :, h, :])[0]
+    dk_rows = np.zeros((len(k_rows_bhj), k.shape[-1]))
+    dv_rows = np.zeros((len(k_rows_bhj), v.shape[-1]))
+    for (b, h) in sorted({(int(b), int(h)) for b, h, _ in k_rows_bhj}):
+        sel = np.nonzero((k_rows_bhj[:, 0] == b) & (k_rows_bhj[:, 1] == h))[0]
+        js = k_rows_bhj[sel, 2]
+        for r0 in range(0, N, oa.ROW_CHUNK):
+            rows = np.arange(r0, min(N, r0 + oa.ROW_CHUNK))
+            p, z, ds = head_rows(b, h, rows)
+            dv_rows[sel] += ((p[:, js] * z[:, js]) * rp).T @ do[b, rows, h, :]
+            dk_rows[sel] += scale * (ds[:, js].T @ q[b, rows, h, :])
+    return dq_rows, dk_rows, dv_rows

@@ -15,9 +15,13 @@ B=4, H=32, N=8192, d=128 causal shape with a 128 x 128 block mask: a band of
 width 1 around the diagonal, one global key block and 10 % random blocks,
 about 18 % of the causal blocks) is timed through fa2_fwd_blocksparse /
 fa2_bwd_blocksparse and reported under "blocksparse", counting the visible
-(query, key) pairs of the active blocks.
+(query, key) pairs of the active blocks. Last, the dense causal workload with
+dropout p = 0.1 on the attention weights (keep matrix from Philox4x64-10,
+regenerated in the backward) is timed through fa2_fwd_dropout /
+fa2_bwd_dropout and reported under "dropout", with the dense FLOP convention.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-varlen] [--no-sparse]
+                  [--no-dropout]
 """
 from __future__ import annotations
 
@@ -205,6 +209,52 @@ def bench_blocksparse(fa2, workloads, steps, warmup):
     }
 
 
+def bench_dropout(fa2, workloads, steps, warmup, p=0.1):
+    """Dense causal workload (B=4, H=32, N=8192, d=128) with dropout p on the attention weights:
+    fa2_fwd_dropout + fa2_bwd_dropout, timed with events; FLOPs as for the dense step."""
+    import torch
+    w = workloads.WORKLOADS[3]
+    B, H, N, d = w.B, w.H, w.N, w.d
+    t = workloads.make_inputs(B, H, N, d, "bf16", seed=w.number, with_dout=True)
+    q, k, v, do = (t[n].cuda() for n in ("q", "k", "v", "dout"))
+    del t
+    out = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws_bytes = fa2.fa2_bwd_workspace_size(B, H, N, d)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    seed, offset = 2024, 0
+
+    def fwd():
+        fa2.fa2_fwd_dropout(q, k, v, out, lse, B, H, N, d, w.scale, 1, -1, -1, None, p, seed, offset, sp)
+
+    def bwd():
+        fa2.fa2_bwd_dropout(q, k, v, out, lse, do, dq, dk, dv, ws, ws_bytes, B, H, N, d, w.scale, 1, -1, -1, None, p,
+                            seed, offset, sp)
+
+    ms = timed([("fwd", fwd), ("bwd", bwd)], steps, warmup, stream)
+    f_fwd = flops(B, H, N, d, True)
+    f_bwd = 2.5 * f_fwd
+    fwd_tf = f_fwd / (ms["fwd"] * 1e-3) / 1e12
+    bwd_tf = f_bwd / (ms["bwd"] * 1e-3) / 1e12
+    step_ms = ms["fwd"] + ms["bwd"]
+    step_tf = (f_fwd + f_bwd) / (step_ms * 1e-3) / 1e12
+    return {
+        "workload": f"bf16 causal attention fwd+bwd with dropout p={p}, B={B} H={H} N={N} d={d}",
+        "fwd_ms": round(ms["fwd"], 4),
+        "bwd_ms": round(ms["bwd"], 4),
+        "step_ms": round(step_ms, 4),
+        "fwd_tflops": round(fwd_tf, 2),
+        "bwd_tflops": round(bwd_tf, 2),
+        "tflops": round(step_tf, 2),
+        "frac_of_peak": round(step_tf / PEAK_BF16_TFLOPS, 4),
+        "fwd_frac_of_peak": round(fwd_tf / PEAK_BF16_TFLOPS, 4),
+        "flop_convention": "as the dense step: forward 4*B*H*N^2*d/2, backward 2.5x",
+    }
+
+
 def recorded_traffic(call):
     """HBM bytes per launch of the dominant kernel from the committed rocprofv3
     FETCH_SIZE / WRITE_SIZE passes (profiles/hbm_traffic.json), reported only if
@@ -237,6 +287,9 @@ def main():
     ap.add_argument("--no-sparse", action="store_true", help="skip the block-sparse measurement")
     ap.add_argument("--sparse-only", action="store_true",
                     help="only time the block-sparse workload (prints its object as the JSON line)")
+    ap.add_argument("--no-dropout", action="store_true", help="skip the dropout measurement")
+    ap.add_argument("--dropout-only", action="store_true",
+                    help="only time the dropout workload (prints its object as the JSON line)")
     ap.add_argument("--atomic-dq", action="store_true",
                     help="time the float-atomic dQ variant of the backward instead of the default passes")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -269,6 +322,9 @@ def main():
         return
     if args.sparse_only:
         print(json.dumps({"blocksparse": bench_blocksparse(fa2, workloads, args.steps, args.warmup)}), flush=True)
+        return
+    if args.dropout_only:
+        print(json.dumps({"dropout": bench_dropout(fa2, workloads, args.steps, args.warmup)}), flush=True)
         return
     w = workloads.WORKLOADS[3]  # B=4, H=32, N=8192, d=128, causal
     B, H, N, d = w.B, w.H, w.N, w.d
@@ -387,6 +443,9 @@ def main():
     if not args.no_sparse:
         rec["blocksparse"] = bench_blocksparse(fa2, workloads, args.steps, args.warmup)
         rec["blocksparse"]["speedup_vs_dense_step"] = round(ms_step / rec["blocksparse"]["step_ms"], 3)
+    if not args.no_dropout:
+        rec["dropout"] = bench_dropout(fa2, workloads, args.steps, args.warmup)
+        rec["dropout"]["slowdown_vs_dense_step"] = round(rec["dropout"]["step_ms"] / ms_step, 3)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(rec), flush=True)

@@ -8,12 +8,13 @@ raises FA2Error; there is no fallback path.
 Low-level functions carry the C names and arguments (fa2_fwd, fa2_fwd_f32,
 fa2_bwd, fa2_bwd_workspace_size, fa2_bwd_prep, fa2_bwd_dkdv, fa2_bwd_dq,
 fa2_fwd_varlen, fa2_bwd_varlen, fa2_fwd_blocksparse, fa2_bwd_blocksparse,
-fa2_status_string, fa2_version); tensors or
+fa2_fwd_dropout, fa2_bwd_dropout, fa2_status_string, fa2_version); tensors or
 raw device addresses (int) are accepted for pointers. The convenience
 functions ``flash_attn_fwd`` / ``flash_attn_bwd`` mirror the parameter list of
-the FlashAttention v2 API on the wmrh.cn article (section 5.1) minus dropout:
-softmax_scale=None (-> 1/sqrt(d)), causal, window_size=(-1, -1), alibi_slopes,
-and deterministic for the backward. ``flash_attn_varlen_fwd`` /
+the FlashAttention v2 API on the wmrh.cn article (section 5.1):
+dropout_p=0.0 (with seed and offset for its keep matrix), softmax_scale=None
+(-> 1/sqrt(d)), causal, window_size=(-1, -1), alibi_slopes, and deterministic
+for the backward. ``flash_attn_varlen_fwd`` /
 ``flash_attn_varlen_bwd`` take sequences packed as [T, H, d] with int32
 boundaries ``cu_seqlens`` [B + 1] (variable-length batches, section 6 of the
 same article). ``flash_attn_blocksparse_fwd`` / ``flash_attn_blocksparse_bwd``
@@ -29,7 +30,7 @@ import os
 __all__ = [
     "FA2Error", "LIB_PATH", "load_library", "fa2_fwd", "fa2_fwd_f32", "fa2_bwd",
     "fa2_bwd_workspace_size", "fa2_bwd_prep", "fa2_bwd_dkdv", "fa2_bwd_dq", "fa2_fwd_varlen", "fa2_bwd_varlen",
-    "fa2_fwd_blocksparse", "fa2_bwd_blocksparse", "fa2_status_string", "fa2_version", "flash_attn_fwd",
+    "fa2_fwd_blocksparse", "fa2_bwd_blocksparse", "fa2_fwd_dropout", "fa2_bwd_dropout", "fa2_status_string", "fa2_version", "flash_attn_fwd",
     "flash_attn_bwd", "flash_attn_varlen_fwd", "flash_attn_varlen_bwd", "flash_attn_blocksparse_fwd",
     "flash_attn_blocksparse_bwd", "BLOCKSPARSE_BLOCK", "FA2_OK", "FA2_ERR_INVALID_ARG", "FA2_ERR_UNSUPPORTED", "FA2_ERR_HIP",
 ]
@@ -49,6 +50,7 @@ _P = ctypes.c_void_p
 _I = ctypes.c_int
 _F = ctypes.c_float
 _L = ctypes.c_longlong
+_U64 = ctypes.c_ulonglong
 
 # C signatures of include/fa2.h
 SIGNATURES = {
@@ -66,6 +68,9 @@ SIGNATURES = {
     "fa2_fwd_blocksparse": ([_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _I, _I, _P, _P, _L, _L, _P], _I),
     "fa2_bwd_blocksparse": ([_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _I, _I, _I, _I, _F, _I, _I, _I,
                              _P, _P, _L, _L, _P], _I),
+    "fa2_fwd_dropout": ([_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _I, _I, _P, _F, _U64, _U64, _P], _I),
+    "fa2_bwd_dropout": ([_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _I, _I, _I, _I, _F, _I, _I, _I,
+                         _P, _F, _U64, _U64, _P], _I),
     "fa2_status_string": ([_I], ctypes.c_char_p),
     "fa2_version": ([], _I),
 }
@@ -217,6 +222,25 @@ def fa2_bwd_blocksparse(q, k, v, out, lse, dout, dq, dk, dv, workspace, workspac
     _check(st, "fa2_bwd_blocksparse")
 
 
+def fa2_fwd_dropout(q, k, v, out, lse, B, H, N, d, softmax_scale, causal, window_left, window_right,
+                    alibi_slopes, dropout_p, seed, offset, stream=None):
+    st = load_library().fa2_fwd_dropout(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), int(B), int(H), int(N),
+                                        int(d), float(softmax_scale), int(causal), int(window_left),
+                                        int(window_right), _ptr(alibi_slopes), float(dropout_p), int(seed),
+                                        int(offset), _stream(stream))
+    _check(st, "fa2_fwd_dropout")
+
+
+def fa2_bwd_dropout(q, k, v, out, lse, dout, dq, dk, dv, workspace, workspace_bytes, B, H, N, d, softmax_scale,
+                    causal, window_left, window_right, alibi_slopes, dropout_p, seed, offset, stream=None):
+    st = load_library().fa2_bwd_dropout(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dout), _ptr(dq),
+                                        _ptr(dk), _ptr(dv), _ptr(workspace), int(workspace_bytes), int(B), int(H),
+                                        int(N), int(d), float(softmax_scale), int(causal), int(window_left),
+                                        int(window_right), _ptr(alibi_slopes), float(dropout_p), int(seed),
+                                        int(offset), _stream(stream))
+    _check(st, "fa2_bwd_dropout")
+
+
 # ------------------------------------------------------------------ convenience wrappers
 
 def _check_tensors(*ts):
@@ -243,8 +267,11 @@ def _slopes(alibi_slopes, H, device):
     return s
 
 
-def flash_attn_fwd(q, k, v, softmax_scale=None, causal=False, window_size=(-1, -1), alibi_slopes=None):
+def flash_attn_fwd(q, k, v, softmax_scale=None, causal=False, window_size=(-1, -1), alibi_slopes=None,
+                   dropout_p=0.0, seed=0, offset=0):
     """Exact attention forward. q, k, v: [B, N, H, d] bf16 or float32 on the GPU.
+    dropout_p > 0 (bf16 only) drops attention weights with the keep matrix of
+    (seed, offset) (see fa2_fwd_dropout in include/fa2.h).
     Returns (out [B, N, H, d], lse [B, H, N] float32, natural log)."""
     import torch
     _check_tensors(q, k, v)
@@ -253,6 +280,12 @@ def flash_attn_fwd(q, k, v, softmax_scale=None, causal=False, window_size=(-1, -
     out = torch.empty_like(q)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     sl = _slopes(alibi_slopes, H, q.device)
+    if dropout_p:
+        if q.dtype != torch.bfloat16:
+            raise FA2Error("dropout takes bf16 tensors")
+        fa2_fwd_dropout(q, k, v, out, lse, B, H, N, d, scale, int(bool(causal)), window_size[0], window_size[1], sl,
+                        dropout_p, seed, offset)
+        return out, lse
     if q.dtype == torch.bfloat16:
         fn = fa2_fwd
     elif q.dtype == torch.float32:
@@ -264,9 +297,9 @@ def flash_attn_fwd(q, k, v, softmax_scale=None, causal=False, window_size=(-1, -
 
 
 def flash_attn_bwd(dout, q, k, v, out, lse, softmax_scale=None, causal=False, window_size=(-1, -1),
-                   alibi_slopes=None, deterministic=False, workspace=None):
+                   alibi_slopes=None, deterministic=False, workspace=None, dropout_p=0.0, seed=0, offset=0):
     """Exact attention backward from the forward's out and lse. bf16 [B, N, H, d] tensors.
-    Returns (dq, dk, dv)."""
+    dropout_p, seed, offset must be those of the forward. Returns (dq, dk, dv)."""
     import torch
     _check_tensors(q, k, v, out, dout)
     if q.dtype != torch.bfloat16:
@@ -278,6 +311,11 @@ def flash_attn_bwd(dout, q, k, v, out, lse, softmax_scale=None, causal=False, wi
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
     sl = _slopes(alibi_slopes, H, q.device)
+    if dropout_p:
+        fa2_bwd_dropout(q, k, v, out, lse, dout, dq, dk, dv, workspace, workspace.numel() * workspace.element_size(),
+                        B, H, N, d, scale, int(bool(causal)), window_size[0], window_size[1], sl, dropout_p, seed,
+                        offset)
+        return dq, dk, dv
     fa2_bwd(q, k, v, out, lse, dout, dq, dk, dv, workspace, workspace.numel() * workspace.element_size(),
             B, H, N, d, scale, int(bool(causal)), window_size[0], window_size[1], sl, int(bool(deterministic)))
     return dq, dk, dv

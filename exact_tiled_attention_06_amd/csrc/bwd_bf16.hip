@@ -34,6 +34,14 @@
 // those. In the key-block pass a list entry also carries which of the
 // workgroup's (up to two) key blocks are active for that query tile, and a
 // wave whose key block is off skips the tile's compute.
+// DROPOUT (deterministic variant, fixed-length dense batches): the keep
+// matrix of the forward is regenerated from the same Philox4x64-10 counters.
+// With Z the keep matrix and r = 1 / (1 - p): dV = (P * Z)^T dO r,
+// dS = P * (Z * dP r - D), and D = rowsum(dO * O) is unchanged (O is the
+// dropped output). The dQ pass has the forward's query-per-lane layout
+// (keep_bits_qlane); the key-block pass has one key per lane and turns the
+// generator's per-query rows into its columns through 128 bytes of LDS per
+// wave (keep_bits_klane).
 #include <type_traits>
 
 #include "common.hpp"
@@ -147,9 +155,10 @@ __device__ __forceinline__ bool bwd_sequence(const BwdParams& p, int rows, bool 
   return true;
 }
 
-template <int D, bool ALIBI, bool DET, int NW, int NST, bool VARLEN, bool SPARSE>
+template <int D, bool ALIBI, bool DET, int NW, int NST, bool VARLEN, bool SPARSE, bool DROPOUT>
 __global__ __launch_bounds__(NW * 64, ((D == 128 && !DET) ? 4 : 8) / NW) void bwd_main_kernel(BwdParams p) {
   static_assert(DET || !(VARLEN || SPARSE), "packed and block-sparse batches use the split dQ pass");
+  static_assert(!DROPOUT || (DET && !VARLEN && !SPARSE), "dropout: split dQ pass, fixed-length dense batches");
   static_assert(!(VARLEN && SPARSE), "packed batches have no block mask");
   using S = BwdShape<D, NW, NST, DET>;
   static_assert(!SPARSE || (S::BK % kSparseBlock == 0 && S::BK <= 2 * kSparseBlock), "one or two key blocks");
@@ -178,6 +187,8 @@ __global__ __launch_bounds__(NW * 64, ((D == 128 && !DET) ? 4 : 8) / NW) void bw
   const int k_last = min(k0 + S::BK, N) - 1;
   const int kw0 = k0 + 32 * w;  // first key of this wave
   const int kj = kw0 + l32;     // key of this lane (MFMA column)
+  const int bh = (int)(stat0 / (N > 0 ? N : 1));            // b * H + h (fixed-length batches)
+  uint32_t* drop_slot = reinterpret_cast<uint32_t*>(smem + S::LDS) + 32 * w;  // DROPOUT: 32 words per wave
 
   // V^T fragments (B operand of dP = dO V^T): lane holds v[kj][16*ks + 8*hh .. +7].
   bf16x8 vf[S::KS];
@@ -342,7 +353,10 @@ __global__ __launch_bounds__(NW * 64, ((D == 128 && !DET) ? 4 : 8) / NW) void bw
           pr[r] = vis ? pr[r] : 0.f;
         }
       }
-      // dP = dO V^T, then dS = P * (dP - D).
+      // Keep bits (dropout) between the two products: S is dead and dP not yet live.
+      const uint32_t keep =
+          DROPOUT ? keep_bits_klane(p.drop_seed, p.drop_offset, p.drop_keep, bh, i0, kw0, l32, hh, drop_slot) : 0u;
+      // dP = dO V^T, then dS = P * (dP - D) (under dropout dS = P * (Z * dP / (1 - p) - D)).
       f32x16 dp = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < S::KS; ++ks) {
@@ -352,14 +366,16 @@ __global__ __launch_bounds__(NW * 64, ((D == 128 && !DET) ? 4 : 8) / NW) void bw
       bf16x8 pb[2], dsb[2];
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        float d8[8];
+        float d8[8], pk[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int r = 8 * kk + e;
-          d8[e] = pr[r] * (dp[r] - del_t[key_of_reg(r, hh)]);
+          const bool kept = !DROPOUT || ((keep >> r) & 1u);
+          const float dpr = DROPOUT ? (kept ? dp[r] * p.drop_scale : 0.f) : dp[r];
+          d8[e] = pr[r] * (dpr - del_t[key_of_reg(r, hh)]);
+          pk[e] = kept ? pr[r] : 0.f;  // dV takes the kept weights; 1 / (1 - p) is applied at the end
         }
-        pb[kk] = pack_bf16x8(pr[8 * kk], pr[8 * kk + 1], pr[8 * kk + 2], pr[8 * kk + 3], pr[8 * kk + 4],
-                             pr[8 * kk + 5], pr[8 * kk + 6], pr[8 * kk + 7]);
+        pb[kk] = pack_bf16x8(pk[0], pk[1], pk[2], pk[3], pk[4], pk[5], pk[6], pk[7]);
         dsb[kk] = pack_bf16x8(d8[0], d8[1], d8[2], d8[3], d8[4], d8[5], d8[6], d8[7]);
       }
       if (!DET) {
@@ -443,7 +459,7 @@ __global__ __launch_bounds__(NW * 64, ((D == 128 && !DET) ? 4 : 8) / NW) void bw
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           xk[e] = (bf16)(dk[mb][4 * a + e] * p.scale);
-          xv[e] = (bf16)(dv[mb][4 * a + e]);
+          xv[e] = (bf16)(DROPOUT ? dv[mb][4 * a + e] * p.drop_scale : dv[mb][4 * a + e]);
         }
         *reinterpret_cast<bf16x4*>(dk_row + 32 * mb + 8 * a + 4 * hh) = xk;
         *reinterpret_cast<bf16x4*>(dv_row + 32 * mb + 8 * a + 4 * hh) = xv;
@@ -458,9 +474,10 @@ __global__ __launch_bounds__(NW * 64, ((D == 128 && !DET) ? 4 : 8) / NW) void bw
 // dP^T = V dO^T put one query per lane (column), so LSE and D are per-lane
 // scalars, and dS^T feeds dQ^T += K^T dS^T as the B operand straight from
 // registers (K^T read transposed from the K tile).
-template <int D, bool ALIBI, int NW, int NST, bool VARLEN, bool SPARSE>
+template <int D, bool ALIBI, int NW, int NST, bool VARLEN, bool SPARSE, bool DROPOUT>
 __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq_det_kernel(BwdParams p) {
   static_assert(!(VARLEN && SPARSE), "packed batches have no block mask");
+  static_assert(!DROPOUT || !(VARLEN || SPARSE), "dropout runs on fixed-length dense batches");
   static_assert(!SPARSE || NW * 32 == kSparseBlock, "a workgroup covers one mask row");
   constexpr int BR = NW * 32, BC = 32;
   constexpr int KS = D / 16, MB = D / 32;
@@ -491,6 +508,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq_det_kernel(BwdParams p
   const int qi = qw0 + l32;
   const bool wave_live = qw0 < N;
   const int wq_last = min(qw0 + 31, N - 1);
+  const int bh = (int)(stat0 / (N > 0 ? N : 1));  // b * H + h (fixed-length batches)
 
   bf16x8 qf[KS], of[KS];
 #pragma unroll
@@ -632,11 +650,16 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq_det_kernel(BwdParams p
         }
       }
       // dQ^T += K^T dS^T: A = K^T (read above), B = dS^T from registers.
+      const uint32_t keep = DROPOUT ? keep_bits_qlane(p.drop_seed, p.drop_offset, p.drop_keep, bh, qi, j0, hh) : 0u;
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
         float d8[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) d8[e] = pr[8 * kk + e] * (dp[8 * kk + e] - delta);
+        for (int e = 0; e < 8; ++e) {
+          const int r = 8 * kk + e;
+          const float dpr = DROPOUT ? (((keep >> r) & 1u) ? dp[r] * p.drop_scale : 0.f) : dp[r];
+          d8[e] = pr[r] * (dpr - delta);
+        }
         const bf16x8 dsb = pack_bf16x8(d8[0], d8[1], d8[2], d8[3], d8[4], d8[5], d8[6], d8[7]);
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) acc[mb] = mfma32(kt[kk][mb], dsb, acc[mb]);
@@ -701,15 +724,16 @@ static hipError_t launch_prep_d(const BwdParams& p, bool zero_acc, hipStream_t s
 }
 
 // Pass 2: the key-block pass (dK, dV; with DET = false also the atomic dQ).
-template <int D, bool ALIBI, bool DET, bool VARLEN, bool SPARSE>
+template <int D, bool ALIBI, bool DET, bool VARLEN, bool SPARSE, bool DROPOUT = false>
 static hipError_t launch_main_d(const BwdParams& p0, hipStream_t stream) {
   // Split dQ pass (DET): deeper Q/dO ring and 8 waves per key block; atomic dQ:
   // 4 waves, 2 stages (its dS^T buffer and dQ step need the room).
   constexpr int NW = DET ? (D == 128 ? FA2_BWD_NW : 4) : 4;
   constexpr int NST = DET ? (D == 128 ? FA2_BWD_NST : 3) : 2;
   using S = BwdShape<D, NW, NST, DET>;
-  auto kmain = bwd_main_kernel<D, ALIBI, DET, NW, NST, VARLEN, SPARSE>;
-  constexpr int lds = S::LDS + (SPARSE ? 2 * (kSparseMaxN / S::BQ) : 0);  // + the query-tile list
+  auto kmain = bwd_main_kernel<D, ALIBI, DET, NW, NST, VARLEN, SPARSE, DROPOUT>;
+  // + the query-tile list (SPARSE) or 32 keep-mask words per wave (DROPOUT)
+  constexpr int lds = S::LDS + (SPARSE ? 2 * (kSparseMaxN / S::BQ) : 0) + (DROPOUT ? NW * 128 : 0);
   static_assert(lds <= 160 * 1024, "LDS budget");
   static bool main_attr = false;
   hipError_t e;
@@ -724,11 +748,11 @@ static hipError_t launch_main_d(const BwdParams& p0, hipStream_t stream) {
 }
 
 // Pass 3 of the split backward: dQ by a sweep over key tiles per query block.
-template <int D, bool ALIBI, bool VARLEN, bool SPARSE>
+template <int D, bool ALIBI, bool VARLEN, bool SPARSE, bool DROPOUT>
 static hipError_t launch_dq_d(const BwdParams& p0, hipStream_t stream) {
   constexpr int DNW = D == 128 ? FA2_DQ_NW : 4;
   constexpr int DNST = FA2_DQ_NST;
-  auto kdq = bwd_dq_det_kernel<D, ALIBI, DNW, DNST, VARLEN, SPARSE>;
+  auto kdq = bwd_dq_det_kernel<D, ALIBI, DNW, DNST, VARLEN, SPARSE, DROPOUT>;
   constexpr int DQ_LDS = DNST * 2 * 32 * D * 2 + (SPARSE ? 2 * (kSparseMaxN / 32) : 0);  // ring (+ tile list)
   static bool dq_attr = false;
   hipError_t e;
@@ -755,30 +779,32 @@ hipError_t launch_bwd_prep(const BwdParams& p, int d, bool zero_acc, hipStream_t
   return d == 128 ? launch_prep_d<128>(p, zero_acc, stream) : launch_prep_d<64>(p, zero_acc, stream);
 }
 
-template <int D, bool VARLEN, bool SPARSE>
+template <int D, bool VARLEN, bool SPARSE, bool DROPOUT>
 static hipError_t launch_dkdv_v(const BwdParams& p, hipStream_t stream) {
-  return p.alibi != nullptr ? launch_main_d<D, true, true, VARLEN, SPARSE>(p, stream)
-                            : launch_main_d<D, false, true, VARLEN, SPARSE>(p, stream);
+  return p.alibi != nullptr ? launch_main_d<D, true, true, VARLEN, SPARSE, DROPOUT>(p, stream)
+                            : launch_main_d<D, false, true, VARLEN, SPARSE, DROPOUT>(p, stream);
 }
 
-template <int D, bool VARLEN, bool SPARSE>
+template <int D, bool VARLEN, bool SPARSE, bool DROPOUT>
 static hipError_t launch_dq_v(const BwdParams& p, hipStream_t stream) {
-  return p.alibi != nullptr ? launch_dq_d<D, true, VARLEN, SPARSE>(p, stream)
-                            : launch_dq_d<D, false, VARLEN, SPARSE>(p, stream);
+  return p.alibi != nullptr ? launch_dq_d<D, true, VARLEN, SPARSE, DROPOUT>(p, stream)
+                            : launch_dq_d<D, false, VARLEN, SPARSE, DROPOUT>(p, stream);
 }
 
 template <int D>
 static hipError_t launch_dkdv_mode(const BwdParams& p, hipStream_t stream) {
-  if (p.block_mask != nullptr) return launch_dkdv_v<D, false, true>(p, stream);
-  if (p.cu_seqlens != nullptr) return launch_dkdv_v<D, true, false>(p, stream);
-  return launch_dkdv_v<D, false, false>(p, stream);
+  if (p.block_mask != nullptr) return launch_dkdv_v<D, false, true, false>(p, stream);
+  if (p.cu_seqlens != nullptr) return launch_dkdv_v<D, true, false, false>(p, stream);
+  if (p.dropout) return launch_dkdv_v<D, false, false, true>(p, stream);
+  return launch_dkdv_v<D, false, false, false>(p, stream);
 }
 
 template <int D>
 static hipError_t launch_dq_mode(const BwdParams& p, hipStream_t stream) {
-  if (p.block_mask != nullptr) return launch_dq_v<D, false, true>(p, stream);
-  if (p.cu_seqlens != nullptr) return launch_dq_v<D, true, false>(p, stream);
-  return launch_dq_v<D, false, false>(p, stream);
+  if (p.block_mask != nullptr) return launch_dq_v<D, false, true, false>(p, stream);
+  if (p.cu_seqlens != nullptr) return launch_dq_v<D, true, false, false>(p, stream);
+  if (p.dropout) return launch_dq_v<D, false, false, true>(p, stream);
+  return launch_dq_v<D, false, false, false>(p, stream);
 }
 
 hipError_t launch_bwd_dkdv(const BwdParams& p, int d, hipStream_t stream) {
@@ -796,7 +822,7 @@ hipError_t launch_bwd_bf16(const BwdParams& p, int d, bool split_dq, hipStream_t
     if ((e = launch_bwd_dkdv(p, d, stream)) != hipSuccess) return e;
     return launch_bwd_dq(p, d, stream);
   }
-  if (p.cu_seqlens != nullptr || p.block_mask != nullptr) return hipErrorInvalidValue;  // split dQ only
+  if (p.cu_seqlens != nullptr || p.block_mask != nullptr || p.dropout) return hipErrorInvalidValue;  // split dQ only
   if ((e = launch_bwd_prep(p, d, true, stream)) != hipSuccess) return e;
   const bool alibi = p.alibi != nullptr;
   if (d == 128) {

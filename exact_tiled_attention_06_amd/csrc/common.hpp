@@ -324,6 +324,110 @@ __device__ __forceinline__ int compact_tiles(uint16_t* list, int t_lo, int t_hi,
 }
 constexpr uint32_t kTileIndexMask = (1u << 14) - 1;
 
+// ---------------------------------------------------------------- dropout
+// Dropout on the attention weights (the dropout_p argument of section 5.1 of
+// the wmrh.cn FlashAttention v2 article; the page names no generator, so the
+// keep matrix is defined here): weight (i, j) of head bh = b * H + h is kept
+// iff a 16-bit value from Philox4x64-10 (Salmon, Moraes, Dror and Shaw,
+// "Parallel random numbers: as easy as 1, 2, 3", SC 2011) is below `keep`.
+// Counter (j / 16, i, bh, 0), key (seed, offset); the 16-bit value of key j
+// is bits 16 * (j % 2) of 32-bit output word (j % 16) / 2 (64-bit words taken
+// low half first). Kept weights are scaled by 1 / (1 - p) where they meet V.
+constexpr uint64_t kPhiloxM0 = 0xD2E7470EE14C6C93ull;
+constexpr uint64_t kPhiloxM1 = 0xCA5A826395121157ull;
+constexpr uint64_t kPhiloxW0 = 0x9E3779B97F4A7C15ull;  // key increments between rounds
+constexpr uint64_t kPhiloxW1 = 0xBB67AE8584CAA73Bull;
+
+// Ten rounds; each multiplies two counter words into 128-bit products and
+// mixes the halves with the other two words and the key.
+__device__ __forceinline__ void philox4x64_10(uint64_t c0, uint64_t c1, uint64_t c2, uint64_t c3, uint64_t k0,
+                                              uint64_t k1, uint32_t (&out)[8]) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r) {
+      k0 += kPhiloxW0;
+      k1 += kPhiloxW1;
+    }
+    const uint64_t lo0 = kPhiloxM0 * c0, hi0 = __umul64hi(kPhiloxM0, c0);
+    const uint64_t lo1 = kPhiloxM1 * c2, hi1 = __umul64hi(kPhiloxM1, c2);
+    const uint64_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
+    c0 = n0;
+    c1 = lo1;
+    c2 = n2;
+    c3 = lo0;
+  }
+  const uint64_t w[4] = {c0, c1, c2, c3};
+#pragma unroll
+  for (int n = 0; n < 4; ++n) {
+    out[2 * n] = (uint32_t)w[n];
+    out[2 * n + 1] = (uint32_t)(w[n] >> 32);
+  }
+}
+
+// The same register of the lane 32 apart (lane l <-> l ^ 32). permlane32_swap
+// returns this lane's value and the other half's value in its two results;
+// which result is which depends on the half, and the XOR takes the other one
+// in either case.
+__device__ __forceinline__ uint32_t from_other_half(uint32_t x) {
+  auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return r[0] ^ r[1] ^ x;
+}
+
+// Two keep bits from a 32-bit word of generator output (low half first).
+__device__ __forceinline__ uint32_t keep2(uint32_t word, uint32_t keep) {
+  return ((word & 0xFFFFu) < keep ? 1u : 0u) | ((word >> 16) < keep ? 2u : 0u);
+}
+
+// Query-per-lane layout (S^T = K Q^T, A-operand row kperm(m)): lane (query i,
+// half hh) holds keys j0 + key_of_reg(r, hh) of a 32-key subtile (j0 % 32 == 0).
+// Returns bit r = keep decision of register r. Half 0 runs the generator for
+// keys j0 .. j0+15, half 1 for j0+16 .. j0+31, and each swaps the 8 values the
+// other half needs: registers 0..7 come from the first call, 8..15 from the second.
+__device__ __forceinline__ uint32_t keep_bits_qlane(uint64_t seed, uint64_t offset, uint32_t keep, int bh, int i,
+                                                    int j0, int hh) {
+  uint32_t x[8];
+  philox4x64_10((uint64_t)(j0 / 16 + hh), (uint64_t)(uint32_t)i, (uint64_t)(uint32_t)bh, 0, seed, offset, x);
+  uint32_t bits = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t recv = from_other_half(hh ? x[k] : x[4 + k]);
+    const uint32_t first = hh ? recv : x[k];       // registers 2k, 2k + 1
+    const uint32_t second = hh ? x[4 + k] : recv;  // registers 8 + 2k, 9 + 2k
+    bits |= keep2(first, keep) << (2 * k);
+    bits |= keep2(second, keep) << (8 + 2 * k);
+  }
+  return bits;
+}
+
+// Key-per-lane layout (S = Q K^T, A-operand row kperm(m)): lane (key kw0 + l32,
+// half hh) holds queries i0 + key_of_reg(r, hh); kw0 % 32 == 0. Each lane runs
+// the generator for query i0 + l32 and keys kw0 + 16 hh .. +15; the halves merge
+// into one 32-bit row mask per query, which goes through `slot` (this wave's 32
+// words of LDS) and comes back as the columns. Returns bit r for register r.
+__device__ __forceinline__ uint32_t keep_bits_klane(uint64_t seed, uint64_t offset, uint32_t keep, int bh, int i0,
+                                                    int kw0, int l32, int hh, uint32_t* slot) {
+  uint32_t x[8];
+  philox4x64_10((uint64_t)(kw0 / 16 + hh), (uint64_t)(uint32_t)(i0 + l32), (uint64_t)(uint32_t)bh, 0, seed, offset,
+                x);
+  uint32_t m = 0;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) m |= keep2(x[k], keep) << (2 * k);
+  const uint32_t other = from_other_half(m);
+  slot[l32] = hh ? (other | (m << 16)) : (m | (other << 16));  // both halves store the same word
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const u32x4 a = *reinterpret_cast<const u32x4*>(slot + 8 * hh);
+  const u32x4 b = *reinterpret_cast<const u32x4*>(slot + 8 * hh + 4);
+  const u32x4 c = *reinterpret_cast<const u32x4*>(slot + 16 + 8 * hh);
+  const u32x4 d = *reinterpret_cast<const u32x4*>(slot + 16 + 8 * hh + 4);
+  const uint32_t rows[16] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3],
+                             c[0], c[1], c[2], c[3], d[0], d[1], d[2], d[3]};
+  uint32_t bits = 0;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) bits |= ((rows[r] >> l32) & 1u) << r;
+  return bits;
+}
+
 struct FwdParams {
   const void* q;
   const void* k;
@@ -343,6 +447,10 @@ struct FwdParams {
   int causal;
   int wl;            // window left (-1 = unbounded)
   int wr;            // window right after the causal clamp (-1 = unbounded)
+  int dropout;       // 0: no dropout; else keep iff generator value < drop_keep
+  uint32_t drop_keep;
+  float drop_scale;  // 1 / (1 - p)
+  uint64_t drop_seed, drop_offset;
 };
 
 struct BwdParams {
@@ -370,6 +478,10 @@ struct BwdParams {
   int causal;
   int wl;
   int wr;
+  int dropout;  // as in FwdParams
+  uint32_t drop_keep;
+  float drop_scale;
+  uint64_t drop_seed, drop_offset;
 };
 
 }  // namespace fa2

@@ -312,6 +312,67 @@ fa2_status_t fa2_bwd_blocksparse(const void* q, const void* k, const void* v, co
   return hip_status(fa2::launch_bwd_bf16(p, d, true, (hipStream_t)stream));
 }
 
+}  // extern "C"
+
+namespace {
+
+// dropout_p in [0, 1): keep threshold floor((1 - p) * 65536 + 0.5) on the
+// generator's 16-bit values, scale 1 / (1 - p). p = 0 keeps every weight and is
+// the dense computation, so it takes the dense kernels.
+fa2_status_t check_dropout(float dropout_p) {
+  if (!(dropout_p >= 0.f) || !(dropout_p < 1.f)) return FA2_ERR_INVALID_ARG;
+  return FA2_OK;
+}
+
+template <typename P>
+void set_dropout(P* p, float dropout_p, unsigned long long seed, unsigned long long offset) {
+  if (dropout_p == 0.f) return;
+  p->dropout = 1;
+  p->drop_keep = (uint32_t)floor((1.0 - (double)dropout_p) * 65536.0 + 0.5);
+  p->drop_scale = 1.0f / (1.0f - dropout_p);
+  p->drop_seed = seed;
+  p->drop_offset = offset;
+}
+
+}  // namespace
+
+extern "C" {
+
+fa2_status_t fa2_fwd_dropout(const void* q, const void* k, const void* v, void* out, float* lse, int B, int H,
+                             int N, int d, float softmax_scale, int causal, int window_left, int window_right,
+                             const float* alibi_slopes, float dropout_p, unsigned long long seed,
+                             unsigned long long offset, void* stream) {
+  bool empty = false;
+  fa2_status_t st = check_common(B, H, N, d, softmax_scale, window_left, window_right, &empty);
+  if (st != FA2_OK) return st;
+  if ((st = check_dropout(dropout_p)) != FA2_OK || empty) return st;
+  if (!q || !k || !v || !out || !lse) return FA2_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(lse))
+    return FA2_ERR_INVALID_ARG;
+  if (alibi_slopes && !aligned4(alibi_slopes)) return FA2_ERR_INVALID_ARG;
+  fa2::FwdParams p = fwd_params(q, k, v, out, lse, B, H, N, softmax_scale, causal, window_left, window_right,
+                                alibi_slopes);
+  set_dropout(&p, dropout_p, seed, offset);
+  return hip_status(fa2::launch_fwd_bf16(p, d, (hipStream_t)stream));
+}
+
+fa2_status_t fa2_bwd_dropout(const void* q, const void* k, const void* v, const void* out, const float* lse,
+                             const void* dout, void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                             int B, int H, int N, int d, float softmax_scale, int causal, int window_left,
+                             int window_right, const float* alibi_slopes, float dropout_p,
+                             unsigned long long seed, unsigned long long offset, void* stream) {
+  fa2::BwdParams p;
+  bool empty = false;
+  fa2_status_t st = check_common(B, H, N, d, softmax_scale, window_left, window_right, &empty);
+  if (st != FA2_OK) return st;
+  if ((st = check_dropout(dropout_p)) != FA2_OK || empty) return st;
+  st = bwd_setup(q, k, v, out, lse, dout, dq, dk, dv, workspace, workspace_bytes, delta_bytes(B, H, N), B, H, N, d,
+                 softmax_scale, causal, window_left, window_right, alibi_slopes, true, true, true, true, &p, &empty);
+  if (st != FA2_OK || empty) return st;
+  set_dropout(&p, dropout_p, seed, offset);
+  return hip_status(fa2::launch_bwd_bf16(p, d, true, (hipStream_t)stream));
+}
+
 const char* fa2_status_string(fa2_status_t s) {
   switch (s) {
     case FA2_OK: return "FA2_OK";

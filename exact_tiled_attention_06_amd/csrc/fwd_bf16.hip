@@ -44,6 +44,12 @@
 //    active key blocks are compacted into a list in LDS (compact_tiles) and
 //    the ring streams only those, so skipped blocks cost neither loads nor
 //    MFMAs. Masks inside a tile are the dense ones.
+//  * DROPOUT: dropout on the attention weights (the dropout_p argument of the
+//    same article, section 5.1). Every lane draws the keep bits of its 16
+//    scores of a 32-key subtile from one Philox4x64-10 call shared with the
+//    other lane half (keep_bits_qlane); the row sum and LSE use the undropped
+//    weights, the P*V operand the kept ones, and 1 / (1 - p) joins 1 / l in
+//    the epilogue.
 #include <type_traits>
 
 #include "common.hpp"
@@ -80,11 +86,18 @@ struct FwdShape {
 #ifndef FA2_FWD_OCC
 #define FA2_FWD_OCC 3
 #endif
-template <int D, int NW, int BC, int NST, bool ALIBI, bool VARLEN, bool SPARSE>
-__global__ __launch_bounds__(NW * 64, (D == 128 ? 4 * FA2_FWD_OCC : 8) / NW)
-__attribute__((amdgpu_waves_per_eu(D == 128 ? FA2_FWD_OCC : 1, D == 128 ? FA2_FWD_OCC : 8))) void fwd_bf16_kernel(FwdParams p) {
+// The dropout variant's generator needs more registers: 2 waves per SIMD.
+template <int D, bool DROPOUT>
+constexpr int fwd_occupancy() {
+  return D == 128 ? (DROPOUT ? 2 : FA2_FWD_OCC) : 2;
+}
+template <int D, int NW, int BC, int NST, bool ALIBI, bool VARLEN, bool SPARSE, bool DROPOUT>
+__global__ __launch_bounds__(NW * 64, (4 * fwd_occupancy<D, DROPOUT>() / NW))
+__attribute__((amdgpu_waves_per_eu(D == 128 ? fwd_occupancy<D, DROPOUT>() : 1, D == 128 ? fwd_occupancy<D, DROPOUT>() : 8)))
+void fwd_bf16_kernel(FwdParams p) {
   using S = FwdShape<D, NW, BC, NST>;
   static_assert(!(VARLEN && SPARSE), "packed batches have no block mask");
+  static_assert(!DROPOUT || !(VARLEN || SPARSE), "dropout runs on fixed-length dense batches");
   static_assert(!SPARSE || S::BR == kSparseBlock, "a workgroup covers one mask row");
   constexpr int PER_WAVE = S::PER_WAVE;
   extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -244,6 +257,12 @@ __attribute__((amdgpu_waves_per_eu(D == 128 ? FA2_FWD_OCC : 1, D == 128 ? FA2_FW
         __builtin_amdgcn_sched_group_barrier(0x008, S::NSUB, 0);                       // MFMAs
       });
 
+      // Keep bits of this lane's scores (bit r: register r of subtile sub).
+      uint32_t keep[S::NSUB];
+#pragma unroll
+      for (int sub = 0; sub < S::NSUB; ++sub)
+        keep[sub] = DROPOUT ? keep_bits_qlane(p.drop_seed, p.drop_offset, p.drop_keep, bh, qi, j0 + 32 * sub, hh) : 0u;
+
       // Bias (ALiBi, in log2 units) and masks; masks only on tiles crossing an edge.
       if (ALIBI) {
 #pragma unroll
@@ -316,7 +335,10 @@ __attribute__((amdgpu_waves_per_eu(D == 128 ? FA2_FWD_OCC : 1, D == 128 ? FA2_FW
           const float x = s[sub][8 * kk + e];
           pv[e] = ALIBI ? fast_exp2(x - m2) : fast_exp2(fmaf(x, p.scale_log2, -m2));
         }
-        const bf16x8 pb = pack_bf16x8(pv[0], pv[1], pv[2], pv[3], pv[4], pv[5], pv[6], pv[7]);
+        float pk[8];  // the P*V operand: the kept weights under dropout
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pk[e] = DROPOUT ? (((keep[sub] >> (8 * kk + e)) & 1u) ? pv[e] : 0.f) : pv[e];
+        const bf16x8 pb = pack_bf16x8(pk[0], pk[1], pk[2], pk[3], pk[4], pk[5], pk[6], pk[7]);
 #pragma unroll
         for (int e = 0; e < 8; ++e) lsum[e & 3] += pv[e];
 #pragma unroll
@@ -342,7 +364,7 @@ __attribute__((amdgpu_waves_per_eu(D == 128 ? FA2_FWD_OCC : 1, D == 128 ? FA2_FW
 
   if (!wave_live) return;
   const float lt = sum_with_other_half((lsum[0] + lsum[1]) + (lsum[2] + lsum[3]));
-  const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+  const float inv = (lt > 0.f ? 1.0f / lt : 0.f) * (DROPOUT ? p.drop_scale : 1.0f);
   if (qi < N) {
     bf16* orow = og + (int64_t)qi * rs;
 #pragma unroll
@@ -361,12 +383,12 @@ __attribute__((amdgpu_waves_per_eu(D == 128 ? FA2_FWD_OCC : 1, D == 128 ? FA2_FW
   }
 }
 
-template <int D, int NW, int BC, int NST, bool ALIBI, bool VARLEN, bool SPARSE>
+template <int D, int NW, int BC, int NST, bool ALIBI, bool VARLEN, bool SPARSE, bool DROPOUT>
 static hipError_t launch_fwd_cfg(const FwdParams& p0, hipStream_t stream) {
   using S = FwdShape<D, NW, BC, NST>;
   FwdParams p = p0;
   p.n_qblocks = VARLEN ? (int)varlen_block_bound(p.N, p.nseq, S::BR) : (p.N + S::BR - 1) / S::BR;
-  auto kern = fwd_bf16_kernel<D, NW, BC, NST, ALIBI, VARLEN, SPARSE>;
+  auto kern = fwd_bf16_kernel<D, NW, BC, NST, ALIBI, VARLEN, SPARSE, DROPOUT>;
   // SPARSE: room for the tile list after the ring (one uint16 per key tile)
   constexpr int lds = S::LDS + (SPARSE ? 2 * (kSparseMaxN / BC) : 0);
   static bool attr_set = false;
@@ -390,18 +412,19 @@ static hipError_t launch_fwd_cfg(const FwdParams& p0, hipStream_t stream) {
 #ifndef FA2_FWD_BC
 #define FA2_FWD_BC 32
 #endif
-template <int D, bool VARLEN, bool SPARSE>
+template <int D, bool VARLEN, bool SPARSE, bool DROPOUT>
 static hipError_t launch_fwd_d(const FwdParams& p, hipStream_t stream) {
   constexpr int NW = SPARSE ? kSparseBlock / 32 : FA2_FWD_NW, NST = FA2_FWD_NST, BC = D == 128 ? FA2_FWD_BC : 64;
-  return p.alibi != nullptr ? launch_fwd_cfg<D, NW, BC, NST, true, VARLEN, SPARSE>(p, stream)
-                            : launch_fwd_cfg<D, NW, BC, NST, false, VARLEN, SPARSE>(p, stream);
+  return p.alibi != nullptr ? launch_fwd_cfg<D, NW, BC, NST, true, VARLEN, SPARSE, DROPOUT>(p, stream)
+                            : launch_fwd_cfg<D, NW, BC, NST, false, VARLEN, SPARSE, DROPOUT>(p, stream);
 }
 
 template <int D>
 static hipError_t launch_fwd_mode(const FwdParams& p, hipStream_t stream) {
-  if (p.block_mask != nullptr) return launch_fwd_d<D, false, true>(p, stream);
-  if (p.cu_seqlens != nullptr) return launch_fwd_d<D, true, false>(p, stream);
-  return launch_fwd_d<D, false, false>(p, stream);
+  if (p.block_mask != nullptr) return launch_fwd_d<D, false, true, false>(p, stream);
+  if (p.cu_seqlens != nullptr) return launch_fwd_d<D, true, false, false>(p, stream);
+  if (p.dropout) return launch_fwd_d<D, false, false, true>(p, stream);
+  return launch_fwd_d<D, false, false, false>(p, stream);
 }
 
 hipError_t launch_fwd_bf16(const FwdParams& p, int d, hipStream_t stream) {

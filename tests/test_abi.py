@@ -33,7 +33,7 @@ def test_header_declares_the_documented_entry_points():
     assert header_functions() == sorted(
         ["fa2_fwd", "fa2_fwd_f32", "fa2_bwd", "fa2_bwd_workspace_size", "fa2_bwd_prep", "fa2_bwd_dkdv",
          "fa2_bwd_dq", "fa2_fwd_varlen", "fa2_bwd_varlen", "fa2_fwd_blocksparse", "fa2_bwd_blocksparse",
-         "fa2_status_string", "fa2_version"])
+         "fa2_fwd_dropout", "fa2_bwd_dropout", "fa2_status_string", "fa2_version"])
 
 
 def test_library_exports_every_header_symbol(lib):
@@ -241,6 +241,52 @@ def test_blocksparse_empty_problem_is_ok(lib, fn):
 def test_blocksparse_backward_checks_workspace(lib):
     args = sparse_args("fa2_bwd_blocksparse", ws_bytes=2 * 300 * 4 - 1)
     assert lib.fa2_bwd_blocksparse(*args) == fa2.FA2_ERR_INVALID_ARG
+
+
+def dropout_args(fn, **over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, lse=FAKE, dout=FAKE, dq=FAKE, dk=FAKE, dv=FAKE, ws=FAKE,
+             ws_bytes=4096, B=1, H=2, N=300, d=128, scale=0.125, causal=1, wl=-1, wr=-1, alibi=None, p=0.1,
+             seed=1, offset=2, stream=None)
+    a.update(over)
+    if fn == "fa2_fwd_dropout":
+        keys = ("q", "k", "v", "out", "lse", "B", "H", "N", "d", "scale", "causal", "wl", "wr", "alibi", "p", "seed",
+                "offset", "stream")
+    else:
+        keys = ("q", "k", "v", "out", "lse", "dout", "dq", "dk", "dv", "ws", "ws_bytes", "B", "H", "N", "d", "scale",
+                "causal", "wl", "wr", "alibi", "p", "seed", "offset", "stream")
+    return [a[k] for k in keys]
+
+
+BAD_DROPOUT = [
+    (dict(p=1.0), fa2.FA2_ERR_INVALID_ARG),
+    (dict(p=-0.25), fa2.FA2_ERR_INVALID_ARG),
+    (dict(p=math.nan), fa2.FA2_ERR_INVALID_ARG),
+    (dict(p=math.inf), fa2.FA2_ERR_INVALID_ARG),
+    (dict(d=96), fa2.FA2_ERR_UNSUPPORTED),
+    (dict(N=-1), fa2.FA2_ERR_INVALID_ARG),
+    (dict(wl=-2), fa2.FA2_ERR_INVALID_ARG),
+    (dict(scale=0.0), fa2.FA2_ERR_INVALID_ARG),
+    (dict(v=None), fa2.FA2_ERR_INVALID_ARG),
+    (dict(lse=MISALIGNED), fa2.FA2_ERR_INVALID_ARG),
+]
+
+
+@pytest.mark.parametrize("fn", ["fa2_fwd_dropout", "fa2_bwd_dropout"])
+@pytest.mark.parametrize("over,status", BAD_DROPOUT)
+def test_dropout_entry_points_reject_bad_arguments(lib, fn, over, status):
+    assert getattr(lib, fn)(*dropout_args(fn, **over)) == status
+
+
+@pytest.mark.parametrize("fn", ["fa2_fwd_dropout", "fa2_bwd_dropout"])
+def test_dropout_empty_problem_is_ok(lib, fn):
+    assert getattr(lib, fn)(*dropout_args(fn, H=0, q=None)) == fa2.FA2_OK
+    # an invalid rate is still rejected on an empty problem
+    assert getattr(lib, fn)(*dropout_args(fn, H=0, p=1.5)) == fa2.FA2_ERR_INVALID_ARG
+
+
+def test_dropout_backward_checks_workspace(lib):
+    args = dropout_args("fa2_bwd_dropout", ws_bytes=2 * 300 * 4 - 1)
+    assert lib.fa2_bwd_dropout(*args) == fa2.FA2_ERR_INVALID_ARG
 
 
 def test_workspace_size(lib):

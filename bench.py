@@ -235,8 +235,7 @@ def bench_dropout(fa2, workloads, steps, warmup, p=0.1):
                             seed, offset, sp)
 
     ms = timed([("fwd", fwd), ("bwd", bwd)], steps, warmup, stream)
-    f_fwd = flops(B, H, N, d, True)
-    f_bwd = 2.5 * f_fwd
+    f_fwd, f_bwd = flops(B, H, N, d, True)
     fwd_tf = f_fwd / (ms["fwd"] * 1e-3) / 1e12
     bwd_tf = f_bwd / (ms["bwd"] * 1e-3) / 1e12
     step_ms = ms["fwd"] + ms["bwd"]

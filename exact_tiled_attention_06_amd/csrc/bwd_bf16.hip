@@ -318,6 +318,7 @@ __global__ __launch_bounds__(NW * 64, ((D == 128 && !DET) ? 4 : 8) / NW) void bw
     const bool off = SPARSE && ((ent >> 14) & (1u << ((32 * w) / kSparseBlock))) == 0;
     const bool skip = off || kw0 >= N || (p.wr >= 0 && i1 + p.wr < kw0) || (p.wl >= 0 && i0 - p.wl > kw0 + 31);
     if (!skip) {
+      // (Pointer-based reads here: absolute addresses measured slower in this kernel.)
       const char* q_t = stage_lds + stg * S::STAGE_BYTES;
       const char* do_t = q_t + S::QT_BYTES;
       const float* lse_t = reinterpret_cast<const float*>(q_t + 2 * S::QT_BYTES);
@@ -590,16 +591,17 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq_det_kernel(BwdParams p
     const int j0 = t * BC, j1 = j0 + BC - 1;
     const bool skip = !wave_live || (p.wr >= 0 && j0 > wq_last + p.wr) || (p.wl >= 0 && j1 < qw0 - p.wl);
     if (!skip) {
-      const char* kb = smem + st * STAGE;
-      const char* vb = kb + TILE;
+      // LDS addresses of this stage's K and V tiles (the dynamic buffer starts at 0:
+      // the launcher checks there is no static LDS).
+      constexpr uint32_t kK = st * STAGE, kV = kK + TILE;
       // S^T = K Q^T and dP^T = V dO^T: rows are keys (A lane m reads row kperm(m)), columns queries.
       // The K and V fragments of step ks + 1 are read while the MFMAs of step ks run.
       f32x16 s = f32x16{}, dp = f32x16{};
       bf16x8 kv[2][2];
       auto kvload = [&](int ks, bf16x8(&dst)[2]) __attribute__((always_inline)) {
         const uint32_t ax = abase ^ (ks << 5);
-        dst[0] = lds_read16(kb, ax);
-        dst[1] = lds_read16(vb, ax);
+        dst[0] = lds_read16_at(kK + ax);
+        dst[1] = lds_read16_at(kV + ax);
       };
       kvload(0, kv[0]);
       static_for<0, KS>([&](auto kc) {
@@ -627,8 +629,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq_det_kernel(BwdParams p
         const int ro = kk * 16 * ROWB;
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
-          const bf16x4 lo = lds_read_tr(kb + ro + tx_lo[mb]);
-          const bf16x4 hi = lds_read_tr(kb + ro + tx_hi[mb]);
+          const bf16x4 lo = lds_read_tr_at(kK + ro + tx_lo[mb]);
+          const bf16x4 hi = lds_read_tr_at(kK + ro + tx_hi[mb]);
           kt[kk][mb] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         }
       }
@@ -710,7 +712,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq_det_kernel(BwdParams p
 
 template <typename K>
 static hipError_t set_lds(K kern, int bytes) {
-  return hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  return e == hipSuccess ? check_lds_at_zero((const void*)kern) : e;
 }
 
 // Pass 1: D = rowsum(dO * O); with zero_acc also clears the float32 dQ accumulator.

@@ -40,6 +40,26 @@ __device__ __forceinline__ bf16x8 lds_read16(const char* base, uint32_t off) {
   return *reinterpret_cast<const bf16x8*>(base + off);
 }
 
+// The same reads at an absolute LDS byte address. Kernels whose only LDS is the
+// dynamic buffer see it at address 0 (their launchers check that the kernel has
+// no static LDS), so a constant part of the address folds into the
+// instruction's offset field instead of costing an add per read.
+__device__ __forceinline__ bf16x8 lds_read16_at(uint32_t addr) {
+  return *reinterpret_cast<const bf16x8 FA2_LDS*>((uintptr_t)addr);
+}
+__device__ __forceinline__ bf16x4 lds_read_tr_at(uint32_t addr) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((bf16x4 FA2_LDS*)((uintptr_t)addr));
+}
+
+// Host side: the absolute-address reads above assume the dynamic LDS buffer
+// starts at address 0, i.e. that the kernel declares no static LDS.
+inline hipError_t check_lds_at_zero(const void* kernel) {
+  hipFuncAttributes fa;
+  hipError_t e = hipFuncGetAttributes(&fa, kernel);
+  if (e != hipSuccess) return e;
+  return fa.sharedSizeBytes == 0 ? hipSuccess : hipErrorInvalidDeviceFunction;
+}
+
 // ds_read_b64_tr_b16: inside each group of 16 lanes, lane i receives four
 // 16-bit values; value e comes from the 8 bytes addressed by group lane
 // 4*e + i/4, element i%4. If group lane j addresses row (r0 + j/4), columns

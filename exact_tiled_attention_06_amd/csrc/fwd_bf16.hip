@@ -228,8 +228,8 @@ void fwd_bf16_kernel(FwdParams p) {
     const int j1 = j0 + BC - 1;
     const bool skip = !wave_live || (p.wr >= 0 && j0 > wq_last + p.wr) || (p.wl >= 0 && j1 < qw0 - p.wl);
     if (!skip) {
-      const char* kb = smem + st * S::STAGE;
-      const char* vb = kb + S::TILE;
+      // Stage st holds K at LDS address st * STAGE and V after it (the dynamic
+      // buffer starts at address 0: the launcher checks there is no static LDS).
 
       // S^T = K Q^T for each 32-key subtile. The K fragments of reduction step
       // ks + 1 are read while the MFMAs of step ks run (two register buffers).
@@ -239,7 +239,9 @@ void fwd_bf16_kernel(FwdParams p) {
       bf16x8 ka[2][S::NSUB];
       auto kload = [&](int ks, bf16x8(&dst)[S::NSUB]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int sub = 0; sub < S::NSUB; ++sub) dst[sub] = lds_read16(kb + sub * 32 * S::ROWB, kbase ^ (ks << 5));
+        for (int sub = 0; sub < S::NSUB; ++sub) {
+          dst[sub] = lds_read16_at(st * S::STAGE + sub * 32 * S::ROWB + (kbase ^ (ks << 5)));
+        }
       };
       kload(0, ka[0]);
       static_for<0, S::KS>([&](auto kc) {
@@ -319,8 +321,8 @@ void fwd_bf16_kernel(FwdParams p) {
         const int rowoff = step * 16 * S::ROWB;
 #pragma unroll
         for (int mb = 0; mb < S::MB; ++mb) {
-          const bf16x4 lo = lds_read_tr(vb + rowoff + vx_lo[mb]);
-          const bf16x4 hi = lds_read_tr(vb + rowoff + vx_hi[mb]);
+          const bf16x4 lo = lds_read_tr_at(st * S::STAGE + S::TILE + rowoff + vx_lo[mb]);
+          const bf16x4 hi = lds_read_tr_at(st * S::STAGE + S::TILE + rowoff + vx_hi[mb]);
           dst[mb] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         }
       };
@@ -394,6 +396,7 @@ static hipError_t launch_fwd_cfg(const FwdParams& p0, hipStream_t stream) {
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (e == hipSuccess) e = check_lds_at_zero((const void*)kern);
     if (e != hipSuccess) return e;
     attr_set = true;
   }

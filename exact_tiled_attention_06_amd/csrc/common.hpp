@@ -69,13 +69,9 @@ __device__ __forceinline__ bf16x4 lds_read_tr(const char* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((bf16x4 FA2_LDS*)(p));
 }
 
-// Value of the lane 32 positions away (lane l <-> l ^ 32), via v_permlane32_swap.
-__device__ __forceinline__ float other_half(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  // lanes 0..31: r[0] = own, r[1] = partner; lanes 32..63: r[0] = partner, r[1] = own
-  return (threadIdx.x & 32) ? __uint_as_float(r[0]) : __uint_as_float(r[1]);
-}
-
+// Row max / row sum across the two lane halves (lane l and l ^ 32) with
+// v_permlane32_swap: its two results hold this lane's value and the other
+// half's (lanes 0..31: own, partner; lanes 32..63: partner, own).
 __device__ __forceinline__ float max_with_other_half(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
@@ -385,9 +381,9 @@ __device__ __forceinline__ void philox4x64_10(uint64_t c0, uint64_t c1, uint64_t
 }
 
 // The same register of the lane 32 apart (lane l <-> l ^ 32). permlane32_swap
-// returns this lane's value and the other half's value in its two results;
-// which result is which depends on the half, and the XOR takes the other one
-// in either case.
+// returns this lane's value and the other half's value in its two results
+// (which is which depends on the half); the XOR of both with the own value is
+// the other half's value.
 __device__ __forceinline__ uint32_t from_other_half(uint32_t x) {
   auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
   return r[0] ^ r[1] ^ x;

@@ -738,12 +738,8 @@ static hipError_t launch_main_d(const BwdParams& p0, hipStream_t stream) {
   // + the query-tile list (SPARSE) or 32 keep-mask words per wave (DROPOUT)
   constexpr int lds = S::LDS + (SPARSE ? 2 * (kSparseMaxN / S::BQ) : 0) + (DROPOUT ? NW * 128 : 0);
   static_assert(lds <= 160 * 1024, "LDS budget");
-  static bool main_attr = false;
-  hipError_t e;
-  if (!main_attr) {
-    if ((e = set_lds(kmain, lds)) != hipSuccess) return e;
-    main_attr = true;
-  }
+  static const hipError_t attr = set_lds(kmain, lds);  // once per kernel; thread-safe initialisation
+  if (attr != hipSuccess) return attr;
   BwdParams p = p0;
   p.nblk = VARLEN ? (int)varlen_block_bound(p.N, p.nseq, S::BK) : (p.N + S::BK - 1) / S::BK;
   hipLaunchKernelGGL(kmain, dim3((unsigned)((int64_t)p.nblk * p.B * p.H)), dim3(S::NT), lds, stream, p);
@@ -757,12 +753,8 @@ static hipError_t launch_dq_d(const BwdParams& p0, hipStream_t stream) {
   constexpr int DNST = FA2_DQ_NST;
   auto kdq = bwd_dq_det_kernel<D, ALIBI, DNW, DNST, VARLEN, SPARSE, DROPOUT>;
   constexpr int DQ_LDS = DNST * 2 * 32 * D * 2 + (SPARSE ? 2 * (kSparseMaxN / 32) : 0);  // ring (+ tile list)
-  static bool dq_attr = false;
-  hipError_t e;
-  if (!dq_attr) {
-    if ((e = set_lds(kdq, DQ_LDS)) != hipSuccess) return e;
-    dq_attr = true;
-  }
+  static const hipError_t attr = set_lds(kdq, DQ_LDS);  // once per kernel; thread-safe initialisation
+  if (attr != hipSuccess) return attr;
   BwdParams p = p0;
   p.nblk = VARLEN ? (int)varlen_block_bound(p.N, p.nseq, DNW * 32) : (p.N + DNW * 32 - 1) / (DNW * 32);
   hipLaunchKernelGGL(kdq, dim3((unsigned)((int64_t)p.nblk * p.B * p.H)), dim3(DNW * 64), DQ_LDS, stream, p);

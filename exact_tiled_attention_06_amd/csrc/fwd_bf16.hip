@@ -393,13 +393,12 @@ static hipError_t launch_fwd_cfg(const FwdParams& p0, hipStream_t stream) {
   auto kern = fwd_bf16_kernel<D, NW, BC, NST, ALIBI, VARLEN, SPARSE, DROPOUT>;
   // SPARSE: room for the tile list after the ring (one uint16 per key tile)
   constexpr int lds = S::LDS + (SPARSE ? 2 * (kSparseMaxN / BC) : 0);
-  static bool attr_set = false;
-  if (!attr_set) {
+  // Once per kernel (thread-safe initialisation of a local static).
+  static const hipError_t attr = [&] {
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-    if (e == hipSuccess) e = check_lds_at_zero((const void*)kern);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+    return e == hipSuccess ? check_lds_at_zero((const void*)kern) : e;
+  }();
+  if (attr != hipSuccess) return attr;
   const int64_t nblk = (int64_t)p.n_qblocks * p.B * p.H;
   hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3(S::NT), lds, stream, p);
   return hipGetLastError();

@@ -22,6 +22,8 @@ fa2_bwd_dropout and reported under "dropout", with the dense FLOP convention.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-varlen] [--no-sparse]
                   [--no-dropout]
+  python bench.py --other-workloads   # the other dense workloads (d=64 non-causal, N=4096 causal,
+                                      # N=16384 window + ALiBi), one JSON line, not the headline
 """
 from __future__ import annotations
 
@@ -254,6 +256,68 @@ def bench_dropout(fa2, workloads, steps, warmup, p=0.1):
     }
 
 
+def visible_pairs(B, H, N, causal, wl, wr):
+    """Number of visible (query, key) pairs under the causal / window rule."""
+    import numpy as np
+    i = np.arange(N, dtype=np.float64)
+    lo = np.zeros(N) if wl < 0 else np.maximum(i - wl, 0)
+    hi = i if causal else (np.full(N, N - 1.0) if wr < 0 else np.minimum(i + wr, N - 1))
+    return float(B * H * (hi - lo + 1).sum())
+
+
+def bench_other_workloads(fa2, workloads, steps, warmup):
+    """fa2_fwd and fa2_bwd on the dense workloads other than the headline one. TFLOP/s in the
+    workload convention (4*B*H*N^2*d, halved for causal; backward 2.5x) and algorithmic (4*d FLOP per
+    visible pair forward, 10*d backward). The d=64 workload (134 MB of inputs) fits the 256 MB
+    Infinity Cache, so it is also timed with a 512 MB write between launches."""
+    import torch
+    res = {}
+    for num in (2, 4, 5):
+        w = workloads.WORKLOADS[num]
+        B, H, N, d = w.B, w.H, w.N, w.d
+        t = workloads.make_inputs(B, H, N, d, "bf16", seed=w.number, with_dout=True)
+        q, k, v, do = (t[n].cuda() for n in ("q", "k", "v", "dout"))
+        del t
+        out = torch.empty_like(q)
+        lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        ws_bytes = fa2.fa2_bwd_workspace_size(B, H, N, d)
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+        sl = workloads.alibi_slopes(H).cuda() if w.alibi else None
+        c, (wl, wr) = int(w.causal), w.window
+        stream = torch.cuda.current_stream()
+        sp = stream.cuda_stream
+
+        def fwd():
+            fa2.fa2_fwd(q, k, v, out, lse, B, H, N, d, w.scale, c, wl, wr, sl, sp)
+
+        def bwd():
+            fa2.fa2_bwd(q, k, v, out, lse, do, dq, dk, dv, ws, ws_bytes, B, H, N, d, w.scale, c, wl, wr, sl, 1, sp)
+
+        ms = timed([("fwd", fwd), ("bwd", bwd)], steps, warmup, stream)
+        nominal = 4.0 * B * H * N * N * d * (0.5 if w.causal else 1.0)
+        pairs = visible_pairs(B, H, N, w.causal, wl, wr)
+        rec = {
+            "workload": w.describe(),
+            "fwd_ms": round(ms["fwd"], 4),
+            "bwd_ms": round(ms["bwd"], 4),
+            "fwd_tflops": round(nominal / (ms["fwd"] * 1e-3) / 1e12, 2),
+            "bwd_tflops": round(2.5 * nominal / (ms["bwd"] * 1e-3) / 1e12, 2),
+            "fwd_tflops_algorithmic": round(4.0 * d * pairs / (ms["fwd"] * 1e-3) / 1e12, 2),
+            "bwd_tflops_algorithmic": round(10.0 * d * pairs / (ms["bwd"] * 1e-3) / 1e12, 2),
+        }
+        if num == 2:
+            flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+            ms_f = timed([("flush", lambda: flush.fill_(1)), ("fwd", fwd)], steps, warmup, stream)
+            rec["fwd_ms_cold_cache"] = round(ms_f["fwd"], 4)
+            rec["fwd_tflops_cold_cache"] = round(nominal / (ms_f["fwd"] * 1e-3) / 1e12, 2)
+            del flush
+        res[w.name] = rec
+        del q, k, v, do, out, lse, dq, dk, dv, ws
+        torch.cuda.empty_cache()
+    return res
+
+
 def recorded_traffic(call):
     """HBM bytes per launch of the dominant kernel from the committed rocprofv3
     FETCH_SIZE / WRITE_SIZE passes (profiles/hbm_traffic.json), reported only if
@@ -289,6 +353,8 @@ def main():
     ap.add_argument("--no-dropout", action="store_true", help="skip the dropout measurement")
     ap.add_argument("--dropout-only", action="store_true",
                     help="only time the dropout workload (prints its object as the JSON line)")
+    ap.add_argument("--other-workloads", action="store_true",
+                    help="only time the other dense workloads (prints their objects as the JSON line)")
     ap.add_argument("--atomic-dq", action="store_true",
                     help="time the float-atomic dQ variant of the backward instead of the default passes")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -321,6 +387,10 @@ def main():
         return
     if args.sparse_only:
         print(json.dumps({"blocksparse": bench_blocksparse(fa2, workloads, args.steps, args.warmup)}), flush=True)
+        return
+    if args.other_workloads:
+        print(json.dumps({"other_workloads": bench_other_workloads(fa2, workloads, args.steps, args.warmup)}),
+              flush=True)
         return
     if args.dropout_only:
         print(json.dumps({"dropout": bench_dropout(fa2, workloads, args.steps, args.warmup)}), flush=True)

@@ -335,14 +335,27 @@ __global__ __launch_bounds__(NW * 64, ((D == 128 && !DET) ? 4 : 8) / NW) void bw
         const bf16x8 bk = lds_read16(k_lds, kb_base ^ (ks << 5));
         s = mfma32(a, bk, s);
       }
-      // P = exp2(S*scale*log2e + bias - LSE*log2e).
+      // P = exp2(S*scale*log2e + bias - LSE*log2e), bias = -slope * |i - j|.
+      float y[16];
+      if (ALIBI && (kw0 + 31 <= i0 || kw0 >= i1)) {
+        // Every key of the wave on one side of every query of the tile: |i - j| = +-(i - j)
+        // and i - j = (i0 + 8 hh - kj) + key_of_reg(r, 0), a constant per register.
+        const float ss = kw0 + 31 <= i0 ? -slope2 : slope2;  // bias = ss * (i - j)
+        const float b0 = ss * (float)(i0 + 8 * hh - kj);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) y[r] = fmaf(s[r], p.scale_log2, fmaf(ss, (float)key_of_reg(r, 0), b0));
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          y[r] = s[r] * p.scale_log2;
+          if (ALIBI) y[r] = fmaf(-slope2, fabsf((float)(i0 + key_of_reg(r, hh) - kj)), y[r]);
+        }
+      }
       float pr[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int qr = key_of_reg(r, hh);  // query row within the block held by register r
-        float y = s[r] * p.scale_log2;
-        if (ALIBI) y = fmaf(-slope2, fabsf((float)(i0 + qr - kj)), y);
-        pr[r] = fast_exp2(fmaf(lse_t[qr], -kLog2e, y));
+        pr[r] = fast_exp2(fmaf(lse_t[qr], -kLog2e, y[r]));
       }
       const bool full = i1 < N && kw0 + 31 < N && (p.wr < 0 || i0 + p.wr >= kw0 + 31) &&
                         (p.wl < 0 || i1 - p.wl <= kw0);
@@ -635,11 +648,21 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq_det_kernel(BwdParams p
         }
       }
       float pr[16];
+      if (ALIBI && (j1 <= qw0 || j0 >= wq_last)) {
+        // Every key of the tile on one side of every query of the wave: |i - j| = +-(j - i)
+        // and j - i = (j0 + 8 hh - qi) + key_of_reg(r, 0), a constant per register.
+        const float ss = j1 <= qw0 ? slope2 : -slope2;  // bias = ss * (j - i)
+        const float b0 = ss * (float)(j0 + 8 * hh - qi);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float y = s[r] * p.scale_log2;
-        if (ALIBI) y = fmaf(-slope2, fabsf((float)(qi - (j0 + key_of_reg(r, hh)))), y);
-        pr[r] = fast_exp2(y - lse2);
+        for (int r = 0; r < 16; ++r)
+          pr[r] = fast_exp2(fmaf(s[r], p.scale_log2, fmaf(ss, (float)key_of_reg(r, 0), b0)) - lse2);
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float y = s[r] * p.scale_log2;
+          if (ALIBI) y = fmaf(-slope2, fabsf((float)(qi - (j0 + key_of_reg(r, hh)))), y);
+          pr[r] = fast_exp2(y - lse2);
+        }
       }
       const bool full = j1 < N && wq_last == qw0 + 31 && (p.wr < 0 || j1 <= qw0 + p.wr) &&
                         (p.wl < 0 || j0 >= wq_last - p.wl);

@@ -267,13 +267,31 @@ void fwd_bf16_kernel(FwdParams p) {
 
       // Bias (ALiBi, in log2 units) and masks; masks only on tiles crossing an edge.
       if (ALIBI) {
+        // bias = -slope * |i - j|. When every key of the tile lies on one side of every
+        // query of the wave, |i - j| = +-(j - i) and j - i = (j0 + 32 sub + 8 hh - i) +
+        // kofs(r) with kofs(r) = key_of_reg(r, hh) - 8 hh a constant: two FMAs per score.
+        const bool below = j1 <= qw0;      // keys <= queries
+        const bool above = j0 >= wq_last;  // keys >= queries
+        if (below || above) {
+          const float ss = below ? slope2 : -slope2;  // bias = ss * (j - i)
 #pragma unroll
-        for (int sub = 0; sub < S::NSUB; ++sub)
+          for (int sub = 0; sub < S::NSUB; ++sub) {
+            const float b0 = ss * (float)(j0 + 32 * sub + 8 * hh - qi);
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = j0 + 32 * sub + key_of_reg(r, hh);
-            s[sub][r] = fmaf(s[sub][r], p.scale_log2, -slope2 * fabsf((float)(qi - key)));
+            for (int r = 0; r < 16; ++r) {
+              const float kofs = (float)(key_of_reg(r, 0));
+              s[sub][r] = fmaf(s[sub][r], p.scale_log2, fmaf(ss, kofs, b0));
+            }
           }
+        } else {
+#pragma unroll
+          for (int sub = 0; sub < S::NSUB; ++sub)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int key = j0 + 32 * sub + key_of_reg(r, hh);
+              s[sub][r] = fmaf(s[sub][r], p.scale_log2, -slope2 * fabsf((float)(qi - key)));
+            }
+        }
       }
       const bool full = j1 < N && (p.wr < 0 || j1 <= qw0 + p.wr) && (p.wl < 0 || j0 >= wq_last - p.wl);
       if (!full) {

@@ -69,6 +69,10 @@ struct BwdShape {
   static constexpr int STAGE_BYTES = 2 * QT_BYTES + 2 * BQ * 4;
   static constexpr int DS_BYTES = DET_ ? 0 : BK * BQ * 2;  // dS^T, [key][query]
   static constexpr int LDS = K_BYTES + NST * STAGE_BYTES + DS_BYTES;
+  // LDS layout: the Q/dO ring first, so that its addresses fit the 16-bit offset
+  // field of the LDS instructions, then the resident K tile, then the dS^T tile.
+  static constexpr int K_OFF = NST * STAGE_BYTES;
+  static_assert(K_OFF % 256 == 0, "K tile offset leaves the row/chunk bits of an address alone");
   static constexpr int DQ_SPLIT = NW / MB;              // waves per d-block in the dQ step
   static constexpr int PER_WAVE = QT_BYTES / (1024 * NW);  // 1 KB direct-load pieces per wave per tile
   static_assert(QT_BYTES % (1024 * NW) == 0, "Q tile must split into 1 KB pieces per wave");
@@ -164,9 +168,9 @@ __global__ __launch_bounds__(NW * 64, ((D == 128 && !DET) ? 4 : 8) / NW) void bw
   static_assert(!SPARSE || (S::BK % kSparseBlock == 0 && S::BK <= 2 * kSparseBlock), "one or two key blocks");
   constexpr int ROWB = 2 * D;
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  char* k_lds = smem;
-  char* stage_lds = smem + S::K_BYTES;
-  char* ds_lds = stage_lds + 2 * S::STAGE_BYTES;
+  char* stage_lds = smem;
+  char* k_lds = smem + S::K_OFF;
+  char* ds_lds = k_lds + S::K_BYTES;
 
   int h, kb, N;
   int64_t tok0, stat0;
@@ -233,7 +237,9 @@ __global__ __launch_bounds__(NW * 64, ((D == 128 && !DET) ? 4 : 8) / NW) void bw
   // Per-lane LDS bases; every read below is base ^ constant or base + constant.
   const int ar = kperm(l32);  // A-operand row (query) for S and dP
   uint32_t qa_base = ar * ROWB + ((hh ^ tile_swz<D>(ar)) << 4);
-  uint32_t kb_base = (32 * w + l32) * ROWB + ((hh ^ tile_swz<D>(l32)) << 4);
+  // K rows of this wave's keys, as LDS addresses (K_OFF is a multiple of 256, so XOR
+  // with a chunk offset below 256 commutes with adding it).
+  uint32_t kb_base = S::K_OFF + (32 * w + l32) * ROWB + ((hh ^ tile_swz<D>(l32)) << 4);
   const int tr0 = 8 * hh + (j >> 2);
   const int c0 = 2 * (g & 1) + ((j & 3) >> 1);
   uint32_t tr_lo = tr0 * ROWB + ((c0 ^ tile_swz<D>(tr0)) << 4) + (j & 1) * 8;
@@ -318,9 +324,10 @@ __global__ __launch_bounds__(NW * 64, ((D == 128 && !DET) ? 4 : 8) / NW) void bw
     const bool off = SPARSE && ((ent >> 14) & (1u << ((32 * w) / kSparseBlock))) == 0;
     const bool skip = off || kw0 >= N || (p.wr >= 0 && i1 + p.wr < kw0) || (p.wl >= 0 && i0 - p.wl > kw0 + 31);
     if (!skip) {
-      // (Pointer-based reads here: absolute addresses measured slower in this kernel.)
+      // LDS addresses (the dynamic buffer starts at 0: the launcher checks there is no
+      // static LDS): this stage's Q and dO tiles; the K tile sits at K_OFF.
+      constexpr uint32_t kQ = stg * S::STAGE_BYTES, kDO = kQ + S::QT_BYTES;
       const char* q_t = stage_lds + stg * S::STAGE_BYTES;
-      const char* do_t = q_t + S::QT_BYTES;
       const float* lse_t = reinterpret_cast<const float*>(q_t + 2 * S::QT_BYTES);
       const float* del_t = lse_t + S::BQ;
 
@@ -331,8 +338,8 @@ __global__ __launch_bounds__(NW * 64, ((D == 128 && !DET) ? 4 : 8) / NW) void bw
       f32x16 s = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < S::KS; ++ks) {
-        const bf16x8 a = lds_read16(q_t, qx[ks]);
-        const bf16x8 bk = lds_read16(k_lds, kb_base ^ (ks << 5));
+        const bf16x8 a = lds_read16_at(kQ + qx[ks]);
+        const bf16x8 bk = lds_read16_at(kb_base ^ (ks << 5));
         s = mfma32(a, bk, s);
       }
       // P = exp2(S*scale*log2e + bias - LSE*log2e), bias = -slope * |i - j|.
@@ -374,7 +381,7 @@ __global__ __launch_bounds__(NW * 64, ((D == 128 && !DET) ? 4 : 8) / NW) void bw
       f32x16 dp = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < S::KS; ++ks) {
-        const bf16x8 ao = lds_read16(do_t, qx[ks]);
+        const bf16x8 ao = lds_read16_at(kDO + qx[ks]);
         dp = mfma32(ao, vf[ks], dp);
       }
       bf16x8 pb[2], dsb[2];
@@ -409,11 +416,11 @@ __global__ __launch_bounds__(NW * 64, ((D == 128 && !DET) ? 4 : 8) / NW) void bw
 #pragma unroll
         for (int mb = 0; mb < S::MB; ++mb) {
           const int ro = kk * 16 * ROWB;
-          const bf16x4 o_lo = lds_read_tr(do_t + ro + tx_lo[mb]);
-          const bf16x4 o_hi = lds_read_tr(do_t + ro + tx_hi[mb]);
+          const bf16x4 o_lo = lds_read_tr_at(kDO + ro + tx_lo[mb]);
+          const bf16x4 o_hi = lds_read_tr_at(kDO + ro + tx_hi[mb]);
           dv[mb] = mfma32(__builtin_shufflevector(o_lo, o_hi, 0, 1, 2, 3, 4, 5, 6, 7), pb[kk], dv[mb]);
-          const bf16x4 q_lo = lds_read_tr(q_t + ro + tx_lo[mb]);
-          const bf16x4 q_hi = lds_read_tr(q_t + ro + tx_hi[mb]);
+          const bf16x4 q_lo = lds_read_tr_at(kQ + ro + tx_lo[mb]);
+          const bf16x4 q_hi = lds_read_tr_at(kQ + ro + tx_hi[mb]);
           dk[mb] = mfma32(__builtin_shufflevector(q_lo, q_hi, 0, 1, 2, 3, 4, 5, 6, 7), dsb[kk], dk[mb]);
         }
       }

@@ -26,6 +26,9 @@ fa2_status_t check_common(int B, int H, int N, int d, float scale, int wl, int w
   if (wl < -1 || wr < -1) return FA2_ERR_INVALID_ARG;
   if (d != 64 && d != 128) return FA2_ERR_UNSUPPORTED;
   if ((int64_t)B * H > INT32_MAX) return FA2_ERR_INVALID_ARG;
+  // The tile loads address a tile's rows as 32-bit byte offsets from its first row:
+  // up to 256 rows of H * d bf16 values must span less than 4 GiB.
+  if ((int64_t)H * d > (int64_t)1 << 22) return FA2_ERR_UNSUPPORTED;
   if ((double)B * N * H * d >= 4.6e18) return FA2_ERR_INVALID_ARG;
   // grid: ceil(N / 64) * B * H blocks must fit a 32-bit grid dimension
   if ((int64_t)((N + 63) / 64) * B * H > (int64_t)UINT32_MAX) return FA2_ERR_UNSUPPORTED;

@@ -36,7 +36,8 @@
  *     problem: FA2_OK, nothing launched, pointers not inspected.
  *   - Alignment: every tensor pointer must be 16-byte aligned.
  *   - Supported shapes: d in {64, 128}; any N >= 1 (ragged tails masked);
- *     B * H <= 2^31 - 1; B * N * H * d < 2^62.
+ *     B * H <= 2^31 - 1; B * N * H * d < 2^62; H * d <= 2^22 (else
+ *     FA2_ERR_UNSUPPORTED: tiles are addressed with 32-bit row offsets).
  */
 #ifndef FA2_H
 #define FA2_H

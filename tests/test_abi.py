@@ -289,6 +289,13 @@ def test_dropout_backward_checks_workspace(lib):
     assert lib.fa2_bwd_dropout(*args) == fa2.FA2_ERR_INVALID_ARG
 
 
+@pytest.mark.parametrize("fn", ["fa2_fwd", "fa2_fwd_f32"])
+def test_forward_rejects_too_many_heads_for_32_bit_tile_offsets(lib, fn):
+    # H * d > 2^22: a 256-row tile would span 4 GiB or more
+    assert getattr(lib, fn)(*fwd_args(H=32769, d=128)) == fa2.FA2_ERR_UNSUPPORTED
+    assert getattr(lib, fn)(*fwd_args(H=65537, d=64)) == fa2.FA2_ERR_UNSUPPORTED
+
+
 def test_workspace_size(lib):
     # delta [B,H,N] + float32 dQ accumulator [B,H,N,d], each rounded up to 256 bytes
     B, H, N, d = 4, 16, 4096, 128

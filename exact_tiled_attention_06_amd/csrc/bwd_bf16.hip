@@ -342,6 +342,19 @@ __global__ __launch_bounds__(NW * 64, ((D == 128 && !DET) ? 4 : 8) / NW) void bw
         const bf16x8 bk = lds_read16_at(kb_base ^ (ks << 5));
         s = mfma32(a, bk, s);
       }
+      // Masks. Dense and packed batches mask S in place (-inf for hidden keys), a branch
+      // that rewrites S where it lies; every row there has a finite LSE. Block-sparse
+      // batches can have rows without a visible key (LSE = -inf) and mask P instead.
+      const bool full = i1 < N && kw0 + 31 < N && (p.wr < 0 || i0 + p.wr >= kw0 + 31) &&
+                        (p.wl < 0 || i1 - p.wl <= kw0);
+      auto visible = [&](int r) __attribute__((always_inline)) {
+        const int q = i0 + key_of_reg(r, hh);
+        return q < N && kj < N && (p.wr < 0 || kj <= q + p.wr) && (p.wl < 0 || kj >= q - p.wl);
+      };
+      if (!SPARSE && !full) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[r] = visible(r) ? s[r] : -INFINITY;
+      }
       // P = exp2(S*scale*log2e + bias - LSE*log2e), bias = -slope * |i - j|.
       float y[16];
       if (ALIBI && (kw0 + 31 <= i0 || kw0 >= i1)) {
@@ -364,15 +377,9 @@ __global__ __launch_bounds__(NW * 64, ((D == 128 && !DET) ? 4 : 8) / NW) void bw
         const int qr = key_of_reg(r, hh);  // query row within the block held by register r
         pr[r] = fast_exp2(fmaf(lse_t[qr], -kLog2e, y[r]));
       }
-      const bool full = i1 < N && kw0 + 31 < N && (p.wr < 0 || i0 + p.wr >= kw0 + 31) &&
-                        (p.wl < 0 || i1 - p.wl <= kw0);
-      if (!full) {
+      if (SPARSE && !full) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int q = i0 + key_of_reg(r, hh);
-          const bool vis = q < N && kj < N && (p.wr < 0 || kj <= q + p.wr) && (p.wl < 0 || kj >= q - p.wl);
-          pr[r] = vis ? pr[r] : 0.f;
-        }
+        for (int r = 0; r < 16; ++r) pr[r] = visible(r) ? pr[r] : 0.f;
       }
       // Keep bits (dropout) between the two products: S is dead and dP not yet live.
       const uint32_t keep =
@@ -537,7 +544,10 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq_det_kernel(BwdParams p
     qf[ks] = qi < N ? *reinterpret_cast<const bf16x8*>(qg + (int64_t)qi * rs + 16 * ks + 8 * hh) : bf16x8{};
     of[ks] = qi < N ? *reinterpret_cast<const bf16x8*>(dog + (int64_t)qi * rs + 16 * ks + 8 * hh) : bf16x8{};
   }
-  const float lse2 = qi < N ? p.lse[stat0 + qi] * kLog2e : INFINITY;
+  // +inf for rows past the end and for rows without a visible key (LSE = -inf): their
+  // masked scores (-inf) then give P = exp2(-inf - lse2) = 0 without a NaN.
+  const float lse_qi = qi < N ? p.lse[stat0 + qi] : -INFINITY;
+  const float lse2 = lse_qi > -INFINITY ? lse_qi * kLog2e : INFINITY;
   const float delta = qi < N ? p.delta[stat0 + qi] : 0.f;
   const float slope2 = ALIBI ? p.alibi[h] * kLog2e : 0.f;
 
@@ -654,6 +664,17 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq_det_kernel(BwdParams p
           kt[kk][mb] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         }
       }
+      // Masks first, on S (-inf for keys the rule hides): a branch that rewrites S in place.
+      const bool full = j1 < N && wq_last == qw0 + 31 && (p.wr < 0 || j1 <= qw0 + p.wr) &&
+                        (p.wl < 0 || j0 >= wq_last - p.wl);
+      if (!full) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = j0 + key_of_reg(r, hh);
+          const bool vis = key < N && qi < N && (p.wr < 0 || key <= qi + p.wr) && (p.wl < 0 || key >= qi - p.wl);
+          s[r] = vis ? s[r] : -INFINITY;
+        }
+      }
       float pr[16];
       if (ALIBI && (j1 <= qw0 || j0 >= wq_last)) {
         // Every key of the tile on one side of every query of the wave: |i - j| = +-(j - i)
@@ -669,16 +690,6 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq_det_kernel(BwdParams p
           float y = s[r] * p.scale_log2;
           if (ALIBI) y = fmaf(-slope2, fabsf((float)(qi - (j0 + key_of_reg(r, hh)))), y);
           pr[r] = fast_exp2(y - lse2);
-        }
-      }
-      const bool full = j1 < N && wq_last == qw0 + 31 && (p.wr < 0 || j1 <= qw0 + p.wr) &&
-                        (p.wl < 0 || j0 >= wq_last - p.wl);
-      if (!full) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = j0 + key_of_reg(r, hh);
-          const bool vis = key < N && qi < N && (p.wr < 0 || key <= qi + p.wr) && (p.wl < 0 || key >= qi - p.wl);
-          pr[r] = vis ? pr[r] : 0.f;
         }
       }
       // dQ^T += K^T dS^T: A = K^T (read above), B = dS^T from registers.

@@ -3,7 +3,9 @@ against the fp64 oracle, every output element checked.
 
 Each case draws B, H, N (1..700, so ragged tails and single-tile problems occur), d,
 causal, the window (none, left only, right only, both), ALiBi and a dropout rate from
-its own seed, so a failure names a reproducible case. Complements the hand-picked
+its own seed, so a failure names a reproducible case. Packed batches (1-6 sequences,
+empty ones included) and block-sparse batches (random masks, shared or per batch,
+rows left without keys) get their own seeded sweeps. Complements the hand-picked
 cases of the other parity files.
 """
 import numpy as np
@@ -83,5 +85,99 @@ def test_seeded_sweep(gpu_lib, case):
     g_ref = given_output(t, to_np(out), o_ref, g_ref, sc, causal, window, sl)
     eg = [rel_to_max(to_np(x), r) for x, r in zip((dq, dk, dv), g_ref)]
     say(f"  O {eo:.3e}  LSE {el:.3e}  grads {eg[0]:.3e} {eg[1]:.3e} {eg[2]:.3e}")
+    assert eo <= TOL_O_BF16 and el <= TOL_LSE
+    assert max(eg) <= TOL_GRAD_REL, eg
+
+
+# ---------------------------------------------------------------- packed and block-sparse batches
+
+def draw_packed(case):
+    r = np.random.default_rng(8000 + case)
+    nseq = int(r.integers(1, 7))
+    lengths = [int(x) for x in r.choice([1, 2, 31, 33, 128, 129, int(r.integers(1, 400))], size=nseq)]
+    if r.integers(0, 4) == 0:
+        lengths[int(r.integers(0, nseq))] = 0  # an empty sequence
+    H, d = int(r.integers(1, 4)), int(r.choice([64, 128]))
+    causal = bool(r.integers(0, 2))
+    kind = int(r.integers(0, 4))
+    wl = int(r.integers(0, 300)) if kind in (1, 3) else -1
+    wr = int(r.integers(0, 300)) if kind in (2, 3) else -1
+    return lengths, H, d, causal, (wl, wr), bool(r.integers(0, 2))
+
+
+@pytest.mark.parametrize("case", range(12))
+def test_seeded_packed_sweep(gpu_lib, case):
+    fa2 = gpu_lib
+    lengths, H, d, causal, window, alibi = draw_packed(case)
+    T = sum(lengths)
+    say(f"packed sweep case {case}: lengths={lengths} H={H} d={d} causal={causal} window={window} alibi={alibi}")
+    if T == 0:
+        lengths[0] = 5
+        T = 5
+    t = workloads.make_varlen_inputs(T, H, d, "bf16", seed=9000 + case, with_dout=True)
+    dev = {k: v.cuda() for k, v in t.items()}
+    cu = workloads.cu_seqlens_from_lengths(lengths)
+    slopes = workloads.alibi_slopes(H) if alibi else None
+    sl = None if slopes is None else slopes.numpy()
+    sc = scale_of(d)
+    out, lse = fa2.flash_attn_varlen_fwd(dev["q"], dev["k"], dev["v"], cu.cuda(), sc, causal, window,
+                                         None if slopes is None else slopes.cuda())
+    dq, dk, dv = fa2.flash_attn_varlen_bwd(dev["dout"], dev["q"], dev["k"], dev["v"], out, lse, cu.cuda(), sc, causal,
+                                           window, None if slopes is None else slopes.cuda())
+    torch.cuda.synchronize()
+    cu_np = cu.numpy()
+    o_ref, lse_ref = oracle.varlen_forward(t["q"], t["k"], t["v"], cu_np, sc, causal, window, sl)
+    g_ref = oracle.varlen_backward(t["q"], t["k"], t["v"], t["dout"], cu_np, sc, causal, window, sl)
+    eo = max_abs(to_np(out), o_ref)
+    el = max_abs(lse.cpu().numpy(), lse_ref)
+    eg = [rel_to_max(to_np(x), r) for x, r in zip((dq, dk, dv), g_ref)]
+    say(f"  O {eo:.3e}  LSE {el:.3e}  grads {eg[0]:.3e} {eg[1]:.3e} {eg[2]:.3e}")
+    assert eo <= TOL_O_BF16 and el <= TOL_LSE
+    assert max(eg) <= TOL_GRAD_REL, eg
+
+
+def draw_sparse(case):
+    r = np.random.default_rng(9500 + case)
+    B, H = int(r.integers(1, 3)), int(r.integers(1, 4))
+    N = int(r.choice([1, 128, 129, 255, int(r.integers(2, 520))]))
+    d = int(r.choice([64, 128]))
+    causal = bool(r.integers(0, 2))
+    kind = int(r.integers(0, 3))
+    window = [(-1, -1), (int(r.integers(0, 300)), 0 if causal else int(r.integers(0, 300))),
+              (int(r.integers(0, 300)), -1)][kind]
+    density = float(r.choice([0.3, 0.6, 1.0]))
+    shared = bool(r.integers(0, 2))
+    return B, H, N, d, causal, window, bool(r.integers(0, 2)), density, shared
+
+
+@pytest.mark.parametrize("case", range(12))
+def test_seeded_blocksparse_sweep(gpu_lib, case):
+    fa2 = gpu_lib
+    B, H, N, d, causal, window, alibi, density, shared = draw_sparse(case)
+    say(f"block-sparse sweep case {case}: B={B} H={H} N={N} d={d} causal={causal} window={window} alibi={alibi} "
+        f"density={density} shared={shared}")
+    t = workloads.make_inputs(B, H, N, d, "bf16", seed=9700 + case, with_dout=True)
+    dev = {k: v.cuda() for k, v in t.items()}
+    nb = -(-N // 128)
+    rng = np.random.default_rng(9900 + case)
+    mask = torch.from_numpy((rng.random((1 if shared else B, H, nb, nb)) < density).astype(np.uint8))
+    slopes = workloads.alibi_slopes(H) if alibi else None
+    sl = None if slopes is None else slopes.numpy()
+    sc = scale_of(d)
+    sl_d = None if slopes is None else slopes.cuda()
+    out, lse = fa2.flash_attn_blocksparse_fwd(dev["q"], dev["k"], dev["v"], mask.cuda(), sc, causal, window, sl_d)
+    dq, dk, dv = fa2.flash_attn_blocksparse_bwd(dev["dout"], dev["q"], dev["k"], dev["v"], out, lse, mask.cuda(), sc,
+                                                causal, window, sl_d)
+    torch.cuda.synchronize()
+    full_mask = mask.expand(B, -1, -1, -1).numpy()
+    o_ref, lse_ref = oracle.blocksparse_forward(t["q"], t["k"], t["v"], full_mask, sc, causal, window, sl)
+    g_ref = oracle.blocksparse_backward(t["q"], t["k"], t["v"], t["dout"], full_mask, sc, causal, window, sl)
+    lse_np = lse.cpu().numpy()
+    empty = np.isneginf(lse_ref)
+    assert np.array_equal(np.isneginf(lse_np), empty)
+    eo = max_abs(to_np(out), o_ref)
+    el = max_abs(lse_np[~empty], lse_ref[~empty])
+    eg = [rel_to_max(to_np(x), r) for x, r in zip((dq, dk, dv), g_ref)]
+    say(f"  empty rows {int(empty.sum())}  O {eo:.3e}  LSE {el:.3e}  grads {eg[0]:.3e} {eg[1]:.3e} {eg[2]:.3e}")
     assert eo <= TOL_O_BF16 and el <= TOL_LSE
     assert max(eg) <= TOL_GRAD_REL, eg

@@ -416,7 +416,7 @@ def main():
     # The backward as its three passes (exactly what fa2_bwd runs by default), so
     # each kernel's duration is measured with its own events.
     def prep():
-        fa2.fa2_bwd_prep(out, do, ws, ws_bytes, B, H, N, d, sp)
+        fa2.fa2_bwd_prep(out, do, lse, ws, ws_bytes, B, H, N, d, scale, sp)
 
     def dkdv():
         fa2.fa2_bwd_dkdv(q, k, v, lse, do, dk, dv, ws, ws_bytes, B, H, N, d, scale, 1, -1, -1, None, sp)

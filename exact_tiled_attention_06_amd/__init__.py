@@ -59,7 +59,7 @@ SIGNATURES = {
     "fa2_bwd_workspace_size": ([_I, _I, _I, _I], ctypes.c_size_t),
     "fa2_bwd": ([_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _I, _I, _I, _I, _F, _I, _I, _I,
                  _P, _I, _P], _I),
-    "fa2_bwd_prep": ([_P, _P, _P, ctypes.c_size_t, _I, _I, _I, _I, _P], _I),
+    "fa2_bwd_prep": ([_P, _P, _P, _P, ctypes.c_size_t, _I, _I, _I, _I, _F, _P], _I),
     "fa2_bwd_dkdv": ([_P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _I, _I, _I, _I, _F, _I, _I, _I, _P, _P], _I),
     "fa2_bwd_dq": ([_P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _I, _I, _I, _I, _F, _I, _I, _I, _P, _P], _I),
     "fa2_fwd_varlen": ([_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _I, _I, _P, _P], _I),
@@ -161,9 +161,9 @@ def fa2_bwd(q, k, v, out, lse, dout, dq, dk, dv, workspace, workspace_bytes, B, 
     _check(st, "fa2_bwd")
 
 
-def fa2_bwd_prep(out, dout, workspace, workspace_bytes, B, H, N, d, stream=None):
-    st = load_library().fa2_bwd_prep(_ptr(out), _ptr(dout), _ptr(workspace), int(workspace_bytes), int(B), int(H),
-                                     int(N), int(d), _stream(stream))
+def fa2_bwd_prep(out, dout, lse, workspace, workspace_bytes, B, H, N, d, softmax_scale, stream=None):
+    st = load_library().fa2_bwd_prep(_ptr(out), _ptr(dout), _ptr(lse), _ptr(workspace), int(workspace_bytes),
+                                     int(B), int(H), int(N), int(d), float(softmax_scale), _stream(stream))
     _check(st, "fa2_bwd_prep")
 
 

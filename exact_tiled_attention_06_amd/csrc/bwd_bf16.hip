@@ -8,8 +8,12 @@
 // dS = P * (dP - D),  dQ = scale * dS K,  dK = scale * dS^T Q.
 //
 // Passes (one stream, in order):
-//  1. bwd_pre_kernel: D = rowsum(dO * O) in float32; zeroes the float32 dQ
-//     accumulator when dQ is accumulated atomically.
+//  1. bwd_pre_kernel: per row -D, D = rowsum(dO * O), and -LSE / scale in
+//     float32; zeroes the float32 dQ accumulator when dQ is accumulated
+//     atomically. The key-block pass starts its S and dP accumulators at these
+//     two values, so that the MFMAs hand back S - LSE / scale and dP - D and
+//     the softmax rebuild needs one multiply per score less, the dS step one
+//     subtraction less.
 //  2. bwd_main_kernel: one workgroup per (batch, head, block of 128 keys) —
 //     the parallelisation over blocks within one head of the FlashAttention-2
 //     paper abstract, item (2), applied to the key axis. Every wavefront owns
@@ -105,7 +109,10 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p, int zero_acc)
     const int64_t i = (row / p.H) % p.N;
     const int64_t b = row / ((int64_t)p.H * p.N);
     const int64_t bhrow = (b * p.H + h) * p.N + i;
-    if (cc == 0) p.delta[bhrow] = acc;
+    if (cc == 0) {
+      p.ndelta[bhrow] = -acc;
+      p.s_init[bhrow] = -p.lse[bhrow] * p.inv_scale;
+    }
     if (zero_acc) {
       f32x4* dst = reinterpret_cast<f32x4*>(p.dq_acc + bhrow * D + cc * 8);
       dst[0] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -184,8 +191,8 @@ __global__ __launch_bounds__(NW * 64, ((D == 128 && !DET) ? 4 : 8) / NW) void bw
   const bf16* kg = (const bf16*)p.k + base;
   const bf16* vg = (const bf16*)p.v + base;
   const bf16* dog = (const bf16*)p.dout + base;
-  const float* lse_g = p.lse + stat0;
-  const float* del_g = p.delta + stat0;
+  const float* sinit_g = p.s_init + stat0;  // -LSE / scale
+  const float* ndel_g = p.ndelta + stat0;   // -D
 
   const int k0 = kb * S::BK;
   const int k_last = min(k0 + S::BK, N) - 1;
@@ -292,7 +299,7 @@ __global__ __launch_bounds__(NW * 64, ((D == 128 && !DET) ? 4 : 8) / NW) void bw
     }
     if (w == 0) {
       const int q = min(i0 + l32, N - 1);
-      const float* src = hh ? del_g + q : lse_g + q;
+      const float* src = hh ? ndel_g + q : sinit_g + q;
       dma4(src, st + 2 * S::QT_BYTES);
     }
   };
@@ -328,14 +335,17 @@ __global__ __launch_bounds__(NW * 64, ((D == 128 && !DET) ? 4 : 8) / NW) void bw
       // static LDS): this stage's Q and dO tiles; the K tile sits at K_OFF.
       constexpr uint32_t kQ = stg * S::STAGE_BYTES, kDO = kQ + S::QT_BYTES;
       const char* q_t = stage_lds + stg * S::STAGE_BYTES;
-      const float* lse_t = reinterpret_cast<const float*>(q_t + 2 * S::QT_BYTES);
-      const float* del_t = lse_t + S::BQ;
+      const float* sinit_t = reinterpret_cast<const float*>(q_t + 2 * S::QT_BYTES);  // -LSE / scale
+      const float* ndel_t = sinit_t + S::BQ;                                           // -D
 
       uint32_t qx[S::KS];
 #pragma unroll
       for (int ks = 0; ks < S::KS; ++ks) qx[ks] = qa_base ^ (ks << 5);
-      // S = Q K^T: rows are queries (A lane m reads row kperm(m)), columns are this wave's keys.
-      f32x16 s = f32x16{};
+      // S - LSE / scale = Q K^T - LSE / scale: rows are queries (A lane m reads row
+      // kperm(m)), columns are this wave's keys; register r holds query key_of_reg(r, hh).
+      f32x16 s;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[r] = sinit_t[key_of_reg(r, hh)];
 #pragma unroll
       for (int ks = 0; ks < S::KS; ++ks) {
         const bf16x8 a = lds_read16_at(kQ + qx[ks]);
@@ -355,7 +365,7 @@ __global__ __launch_bounds__(NW * 64, ((D == 128 && !DET) ? 4 : 8) / NW) void bw
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[r] = visible(r) ? s[r] : -INFINITY;
       }
-      // P = exp2(S*scale*log2e + bias - LSE*log2e), bias = -slope * |i - j|.
+      // P = exp2((S - LSE / scale) * scale * log2e + bias), bias = -slope * |i - j|.
       float y[16];
       if (ALIBI && (kw0 + 31 <= i0 || kw0 >= i1)) {
         // Every key of the wave on one side of every query of the tile: |i - j| = +-(i - j)
@@ -373,10 +383,7 @@ __global__ __launch_bounds__(NW * 64, ((D == 128 && !DET) ? 4 : 8) / NW) void bw
       }
       float pr[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int qr = key_of_reg(r, hh);  // query row within the block held by register r
-        pr[r] = fast_exp2(fmaf(lse_t[qr], -kLog2e, y[r]));
-      }
+      for (int r = 0; r < 16; ++r) pr[r] = fast_exp2(y[r]);
       if (SPARSE && !full) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) pr[r] = visible(r) ? pr[r] : 0.f;
@@ -384,8 +391,11 @@ __global__ __launch_bounds__(NW * 64, ((D == 128 && !DET) ? 4 : 8) / NW) void bw
       // Keep bits (dropout) between the two products: S is dead and dP not yet live.
       const uint32_t keep =
           DROPOUT ? keep_bits_klane(p.drop_seed, p.drop_offset, p.drop_keep, bh, i0, kw0, l32, hh, drop_slot) : 0u;
-      // dP = dO V^T, then dS = P * (dP - D) (under dropout dS = P * (Z * dP / (1 - p) - D)).
-      f32x16 dp = f32x16{};
+      // dP - D = dO V^T - D, then dS = P * (dP - D) (under dropout the accumulators start
+      // at 0 and dS = P * (Z * dP / (1 - p) - D)).
+      f32x16 dp;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dp[r] = DROPOUT ? 0.f : ndel_t[key_of_reg(r, hh)];
 #pragma unroll
       for (int ks = 0; ks < S::KS; ++ks) {
         const bf16x8 ao = lds_read16_at(kDO + qx[ks]);
@@ -399,8 +409,7 @@ __global__ __launch_bounds__(NW * 64, ((D == 128 && !DET) ? 4 : 8) / NW) void bw
         for (int e = 0; e < 8; ++e) {
           const int r = 8 * kk + e;
           const bool kept = !DROPOUT || ((keep >> r) & 1u);
-          const float dpr = DROPOUT ? (kept ? dp[r] * p.drop_scale : 0.f) : dp[r];
-          d8[e] = pr[r] * (dpr - del_t[key_of_reg(r, hh)]);
+          d8[e] = DROPOUT ? pr[r] * ((kept ? dp[r] * p.drop_scale : 0.f) + ndel_t[key_of_reg(r, hh)]) : pr[r] * dp[r];
           pk[e] = kept ? pr[r] : 0.f;  // dV takes the kept weights; 1 / (1 - p) is applied at the end
         }
         pb[kk] = pack_bf16x8(pk[0], pk[1], pk[2], pk[3], pk[4], pk[5], pk[6], pk[7]);
@@ -548,7 +557,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq_det_kernel(BwdParams p
   // masked scores (-inf) then give P = exp2(-inf - lse2) = 0 without a NaN.
   const float lse_qi = qi < N ? p.lse[stat0 + qi] : -INFINITY;
   const float lse2 = lse_qi > -INFINITY ? lse_qi * kLog2e : INFINITY;
-  const float delta = qi < N ? p.delta[stat0 + qi] : 0.f;
+  const float ndelta = qi < N ? p.ndelta[stat0 + qi] : 0.f;  // -D
   const float slope2 = ALIBI ? p.alibi[h] * kLog2e : 0.f;
 
   int kv_lo = 0, kv_hi = N;
@@ -701,7 +710,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq_det_kernel(BwdParams p
         for (int e = 0; e < 8; ++e) {
           const int r = 8 * kk + e;
           const float dpr = DROPOUT ? (((keep >> r) & 1u) ? dp[r] * p.drop_scale : 0.f) : dp[r];
-          d8[e] = pr[r] * (dpr - delta);
+          d8[e] = pr[r] * (dpr + ndelta);
         }
         const bf16x8 dsb = pack_bf16x8(d8[0], d8[1], d8[2], d8[3], d8[4], d8[5], d8[6], d8[7]);
 #pragma unroll

@@ -480,7 +480,8 @@ struct BwdParams {
   void* dk;
   void* dv;
   float* dq_acc;  // [B, H, N, d] float32 workspace
-  float* delta;   // [B, H, N] float32 workspace
+  float* ndelta;  // [B, H, N] float32 workspace: -D, D = rowsum(dO * O)
+  float* s_init;  // [B, H, N] float32 workspace: -LSE / scale, where the key-block pass starts S
   const float* alibi;
   int B, H, N;       // packed batches: B = 1, N = total tokens
   int nblk;          // blocks per head of the kernel being launched (packed: virtual-block bound)
@@ -491,6 +492,7 @@ struct BwdParams {
   int nbk;
   float scale;
   float scale_log2;
+  float inv_scale;
   int causal;
   int wl;
   int wr;

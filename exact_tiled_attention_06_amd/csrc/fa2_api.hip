@@ -86,7 +86,7 @@ fa2_status_t fa2_fwd_f32(const float* q, const float* k, const float* v, float* 
 size_t fa2_bwd_workspace_size(int B, int H, int N, int d) {
   if (B <= 0 || H <= 0 || N <= 0 || (d != 64 && d != 128)) return 0;
   const size_t rows = (size_t)B * H * N;
-  return align256(rows * sizeof(float)) + align256(rows * d * sizeof(float));
+  return 2 * align256(rows * sizeof(float)) + align256(rows * d * sizeof(float));
 }
 
 }  // extern "C"
@@ -103,7 +103,7 @@ fa2_status_t bwd_setup(const void* q, const void* k, const void* v, const void* 
   fa2_status_t st = check_common(B, H, N, d, scale, wl, wr, empty);
   if (st != FA2_OK || *empty) return st;
   const void* needed[] = {need_qkv ? q : dout, need_qkv ? k : dout, need_qkv ? v : dout,
-                          need_qkv ? (const void*)lse : dout, need_out ? out : dout, dout,
+                          (const void*)lse, need_out ? out : dout, dout,
                           need_dq ? dq : dout, need_dkdv ? dk : dout, need_dkdv ? dv : dout, workspace};
   for (const void* ptr : needed)
     if (!ptr || !aligned16(ptr)) return FA2_ERR_INVALID_ARG;
@@ -113,20 +113,24 @@ fa2_status_t bwd_setup(const void* q, const void* k, const void* v, const void* 
   *p = fa2::BwdParams{};
   p->q = q; p->k = k; p->v = v; p->o = out; p->lse = lse; p->dout = dout;
   p->dq = dq; p->dk = dk; p->dv = dv;
-  p->delta = reinterpret_cast<float*>(const_cast<void*>(workspace));
-  p->dq_acc = reinterpret_cast<float*>(reinterpret_cast<char*>(const_cast<void*>(workspace)) +
-                                       align256(rows * sizeof(float)));
+  // Workspace: -D per row, -LSE / scale per row, then (atomic dQ only) the dQ accumulator.
+  char* ws = reinterpret_cast<char*>(const_cast<void*>(workspace));
+  p->ndelta = reinterpret_cast<float*>(ws);
+  p->s_init = reinterpret_cast<float*>(ws + align256(rows * sizeof(float)));
+  p->dq_acc = reinterpret_cast<float*>(ws + 2 * align256(rows * sizeof(float)));
   p->alibi = alibi;
   p->B = B; p->H = H; p->N = N;
   p->scale = scale;
   p->scale_log2 = scale * fa2::kLog2e;
+  p->inv_scale = 1.0f / scale;
   p->causal = causal ? 1 : 0;
   p->wl = wl;
   p->wr = causal ? 0 : wr;
   return FA2_OK;
 }
 
-size_t delta_bytes(int B, int H, int N) { return align256((size_t)B * H * N * sizeof(float)); }
+// Workspace of the split backward: -D and -LSE / scale, one float each per row.
+size_t stat_bytes(int B, int H, int N) { return 2 * align256((size_t)B * H * N * sizeof(float)); }
 
 fa2_status_t hip_status(hipError_t e) { return e == hipSuccess ? FA2_OK : FA2_ERR_HIP; }
 
@@ -150,7 +154,7 @@ fa2_status_t fa2_bwd(const void* q, const void* k, const void* v, const void* ou
   }
   fa2::BwdParams p;
   bool empty = false;
-  const size_t need = split_dq ? delta_bytes(B, H, N) : fa2_bwd_workspace_size(B, H, N, d);
+  const size_t need = split_dq ? stat_bytes(B, H, N) : fa2_bwd_workspace_size(B, H, N, d);
   fa2_status_t st = bwd_setup(q, k, v, out, lse, dout, dq, dk, dv, workspace, workspace_bytes, need, B, H, N, d,
                               softmax_scale, causal, window_left, window_right, alibi_slopes, true, true, true,
                               true, &p, &empty);
@@ -158,13 +162,13 @@ fa2_status_t fa2_bwd(const void* q, const void* k, const void* v, const void* ou
   return hip_status(fa2::launch_bwd_bf16(p, d, split_dq, (hipStream_t)stream));
 }
 
-fa2_status_t fa2_bwd_prep(const void* out, const void* dout, void* workspace, size_t workspace_bytes, int B, int H,
-                          int N, int d, void* stream) {
+fa2_status_t fa2_bwd_prep(const void* out, const void* dout, const float* lse, void* workspace,
+                          size_t workspace_bytes, int B, int H, int N, int d, float softmax_scale, void* stream) {
   fa2::BwdParams p;
   bool empty = false;
-  fa2_status_t st = bwd_setup(nullptr, nullptr, nullptr, out, nullptr, dout, nullptr, nullptr, nullptr, workspace,
-                              workspace_bytes, delta_bytes(B, H, N), B, H, N, d, 1.0f, 0, -1, -1, nullptr, false,
-                              true, false, false, &p, &empty);
+  fa2_status_t st = bwd_setup(nullptr, nullptr, nullptr, out, lse, dout, nullptr, nullptr, nullptr, workspace,
+                              workspace_bytes, stat_bytes(B, H, N), B, H, N, d, softmax_scale, 0, -1, -1, nullptr,
+                              false, true, false, false, &p, &empty);
   if (st != FA2_OK || empty) return st;
   return hip_status(fa2::launch_bwd_prep(p, d, false, (hipStream_t)stream));
 }
@@ -176,7 +180,7 @@ fa2_status_t fa2_bwd_dkdv(const void* q, const void* k, const void* v, const flo
   fa2::BwdParams p;
   bool empty = false;
   fa2_status_t st = bwd_setup(q, k, v, nullptr, lse, dout, nullptr, dk, dv, workspace, workspace_bytes,
-                              delta_bytes(B, H, N), B, H, N, d, softmax_scale, causal, window_left, window_right,
+                              stat_bytes(B, H, N), B, H, N, d, softmax_scale, causal, window_left, window_right,
                               alibi_slopes, true, false, false, true, &p, &empty);
   if (st != FA2_OK || empty) return st;
   return hip_status(fa2::launch_bwd_dkdv(p, d, (hipStream_t)stream));
@@ -189,7 +193,7 @@ fa2_status_t fa2_bwd_dq(const void* q, const void* k, const void* v, const float
   fa2::BwdParams p;
   bool empty = false;
   fa2_status_t st = bwd_setup(q, k, v, nullptr, lse, dout, dq, nullptr, nullptr, workspace, workspace_bytes,
-                              delta_bytes(B, H, N), B, H, N, d, softmax_scale, causal, window_left, window_right,
+                              stat_bytes(B, H, N), B, H, N, d, softmax_scale, causal, window_left, window_right,
                               alibi_slopes, true, false, true, false, &p, &empty);
   if (st != FA2_OK || empty) return st;
   return hip_status(fa2::launch_bwd_dq(p, d, (hipStream_t)stream));
@@ -247,7 +251,7 @@ fa2_status_t fa2_bwd_varlen(const void* q, const void* k, const void* v, const v
   fa2_status_t st = check_varlen(cu_seqlens, B, total_tokens, H, d, softmax_scale, window_left, window_right, &empty);
   if (st != FA2_OK || empty) return st;
   fa2::BwdParams p;
-  st = bwd_setup(q, k, v, out, lse, dout, dq, dk, dv, workspace, workspace_bytes, delta_bytes(1, H, total_tokens), 1,
+  st = bwd_setup(q, k, v, out, lse, dout, dq, dk, dv, workspace, workspace_bytes, stat_bytes(1, H, total_tokens), 1,
                  H, total_tokens, d, softmax_scale, causal, window_left, window_right, alibi_slopes, true, true, true,
                  true, &p, &empty);
   if (st != FA2_OK || empty) return st;
@@ -308,7 +312,7 @@ fa2_status_t fa2_bwd_blocksparse(const void* q, const void* k, const void* v, co
   fa2_status_t st = check_common(B, H, N, d, softmax_scale, window_left, window_right, &empty);
   if (st != FA2_OK || empty) return st;
   if ((st = check_block_mask(block_mask, N, mask_stride_b, mask_stride_h)) != FA2_OK) return st;
-  st = bwd_setup(q, k, v, out, lse, dout, dq, dk, dv, workspace, workspace_bytes, delta_bytes(B, H, N), B, H, N, d,
+  st = bwd_setup(q, k, v, out, lse, dout, dq, dk, dv, workspace, workspace_bytes, stat_bytes(B, H, N), B, H, N, d,
                  softmax_scale, causal, window_left, window_right, alibi_slopes, true, true, true, true, &p, &empty);
   if (st != FA2_OK || empty) return st;
   set_block_mask(&p, block_mask, N, mask_stride_b, mask_stride_h);
@@ -369,7 +373,7 @@ fa2_status_t fa2_bwd_dropout(const void* q, const void* k, const void* v, const 
   fa2_status_t st = check_common(B, H, N, d, softmax_scale, window_left, window_right, &empty);
   if (st != FA2_OK) return st;
   if ((st = check_dropout(dropout_p)) != FA2_OK || empty) return st;
-  st = bwd_setup(q, k, v, out, lse, dout, dq, dk, dv, workspace, workspace_bytes, delta_bytes(B, H, N), B, H, N, d,
+  st = bwd_setup(q, k, v, out, lse, dout, dq, dk, dv, workspace, workspace_bytes, stat_bytes(B, H, N), B, H, N, d,
                  softmax_scale, causal, window_left, window_right, alibi_slopes, true, true, true, true, &p, &empty);
   if (st != FA2_OK || empty) return st;
   set_dropout(&p, dropout_p, seed, offset);

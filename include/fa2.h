@@ -78,12 +78,13 @@ fa2_status_t fa2_fwd_f32(const float* q, const float* k, const float* v, float* 
                          void* stream);
 
 /*
- * Bytes of device workspace for the backward at this shape: the per-row
- * D = rowsum(dO * O), float32 [B, H, N], at offset 0, then a float32 dQ
- * accumulator [B, H, N, d] used only by the atomic variant (each part rounded
- * up to 256 bytes). The default fa2_bwd and the three pass entry points below
- * only touch the first part, round_up(4 * B * H * N, 256) bytes, and accept a
- * workspace of that size. Returns 0 for an empty or invalid shape.
+ * Bytes of device workspace for the backward at this shape: two per-row float32
+ * arrays [B, H, N], -D (D = rowsum(dO * O)) at offset 0 and -LSE / scale after
+ * it, then a float32 dQ accumulator [B, H, N, d] used only by the atomic
+ * variant (each part rounded up to 256 bytes). The default fa2_bwd and the
+ * three pass entry points below only touch the two per-row arrays,
+ * 2 * round_up(4 * B * H * N, 256) bytes, and accept a workspace of that size.
+ * Returns 0 for an empty or invalid shape.
  */
 size_t fa2_bwd_workspace_size(int B, int H, int N, int d);
 
@@ -117,18 +118,22 @@ fa2_status_t fa2_bwd(const void* q, const void* k, const void* v, const void* ou
  * calls, for callers that schedule them themselves (for instance the dK/dV
  * and dQ passes on two streams: both depend only on fa2_bwd_prep). Arguments
  * mean what they mean for fa2_bwd; the same workspace (at least
- * round_up(4 * B * H * N, 256) bytes) must be passed to all three, and
- * fa2_bwd_prep must have completed before the other two read it.
- *   fa2_bwd_prep: D = rowsum(dO * O) into the workspace.
+ * 2 * round_up(4 * B * H * N, 256) bytes) must be passed to all three, with the
+ * same lse and softmax_scale, and fa2_bwd_prep must have completed before the
+ * other two read it.
+ *   fa2_bwd_prep: -D (D = rowsum(dO * O)) and -LSE / scale per row into the
+ *                 workspace.
  *   fa2_bwd_dkdv: dK and dV, one pass over query blocks per key block
- *                 (recomputes P and dS; reads D).
+ *                 (recomputes P and dS; reads both workspace arrays, which
+ *                 stand in for lse there; lse is still checked).
  *   fa2_bwd_dq:   dQ, one pass over key tiles per query block (recomputes P and
- *                 dS; reads D); no atomics, bitwise repeatable.
+ *                 dS; reads lse and -D); no atomics, bitwise repeatable.
  * Source: the backward-by-recomputation of "AI基础 | Flash Attention"
  * (section 反向传播), split by output.
  */
-fa2_status_t fa2_bwd_prep(const void* out, const void* dout, void* workspace, size_t workspace_bytes,
-                          int B, int H, int N, int d, void* stream);
+fa2_status_t fa2_bwd_prep(const void* out, const void* dout, const float* lse, void* workspace,
+                          size_t workspace_bytes, int B, int H, int N, int d, float softmax_scale,
+                          void* stream);
 fa2_status_t fa2_bwd_dkdv(const void* q, const void* k, const void* v, const float* lse,
                           const void* dout, void* dk, void* dv, const void* workspace,
                           size_t workspace_bytes, int B, int H, int N, int d, float softmax_scale,
@@ -172,7 +177,7 @@ fa2_status_t fa2_fwd_varlen(const void* q, const void* k, const void* v, void* o
 
 /*
  * Backward of fa2_fwd_varlen (same arguments, plus dout, dq, dk, dv and a
- * workspace of at least round_up(4 * H * total_tokens, 256) bytes, which
+ * workspace of at least 2 * round_up(4 * H * total_tokens, 256) bytes, which
  * fa2_bwd_workspace_size(1, H, total_tokens, d) covers). Always the
  * atomic-free algorithm (D pass, dK/dV pass, dQ pass): bitwise repeatable.
  */
@@ -202,7 +207,8 @@ fa2_status_t fa2_bwd_varlen(const void* q, const void* k, const void* v, const v
  * Layouts, other arguments and errors as for fa2_fwd / fa2_bwd. N above 65536
  * is FA2_ERR_UNSUPPORTED; a null block_mask or a negative stride is
  * FA2_ERR_INVALID_ARG. The backward is always the atomic-free algorithm
- * (bitwise repeatable) and needs round_up(4 * B * H * N, 256) workspace bytes.
+ * (bitwise repeatable) and needs 2 * round_up(4 * B * H * N, 256) workspace
+ * bytes.
  */
 #define FA2_BLOCKSPARSE_BLOCK 128
 
@@ -241,7 +247,7 @@ fa2_status_t fa2_bwd_blocksparse(const void* q, const void* k, const void* v, co
  * callers advance `offset` between calls that share a seed. Layouts, other
  * arguments and errors as for fa2_fwd / fa2_bwd; the backward is the
  * atomic-free algorithm (bitwise repeatable) and needs
- * round_up(4 * B * H * N, 256) workspace bytes. Fixed-length dense batches
+ * 2 * round_up(4 * B * H * N, 256) workspace bytes. Fixed-length dense batches
  * only (no packed or block-sparse variant).
  */
 fa2_status_t fa2_fwd_dropout(const void* q, const void* k, const void* v, void* out, float* lse,

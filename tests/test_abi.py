@@ -133,12 +133,14 @@ def test_backward_empty_problem_is_ok(lib):
 
 
 def test_pass_entry_points_reject_bad_arguments(lib):
-    ws = 256
-    # prep: null dout, bad d, too-small workspace
-    assert lib.fa2_bwd_prep(FAKE, None, FAKE, ws, 1, 2, 16, 64, None) == fa2.FA2_ERR_INVALID_ARG
-    assert lib.fa2_bwd_prep(FAKE, FAKE, FAKE, ws, 1, 2, 16, 96, None) == fa2.FA2_ERR_UNSUPPORTED
-    assert lib.fa2_bwd_prep(FAKE, FAKE, FAKE, 8, 1, 2, 16, 64, None) == fa2.FA2_ERR_INVALID_ARG
-    assert lib.fa2_bwd_prep(FAKE, FAKE, FAKE, ws, 0, 2, 16, 64, None) == fa2.FA2_OK
+    ws = 512
+    # prep: null dout, null lse, bad d, bad scale, too-small workspace
+    assert lib.fa2_bwd_prep(FAKE, None, FAKE, FAKE, ws, 1, 2, 16, 64, 0.125, None) == fa2.FA2_ERR_INVALID_ARG
+    assert lib.fa2_bwd_prep(FAKE, FAKE, None, FAKE, ws, 1, 2, 16, 64, 0.125, None) == fa2.FA2_ERR_INVALID_ARG
+    assert lib.fa2_bwd_prep(FAKE, FAKE, FAKE, FAKE, ws, 1, 2, 16, 96, 0.125, None) == fa2.FA2_ERR_UNSUPPORTED
+    assert lib.fa2_bwd_prep(FAKE, FAKE, FAKE, FAKE, ws, 1, 2, 16, 64, 0.0, None) == fa2.FA2_ERR_INVALID_ARG
+    assert lib.fa2_bwd_prep(FAKE, FAKE, FAKE, FAKE, 256, 1, 2, 16, 64, 0.125, None) == fa2.FA2_ERR_INVALID_ARG
+    assert lib.fa2_bwd_prep(FAKE, FAKE, FAKE, FAKE, ws, 0, 2, 16, 64, 0.125, None) == fa2.FA2_OK
     args = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws, 1, 2, 16, 64, 0.125, 1, -1, -1, None, None]
     assert lib.fa2_bwd_dkdv(*args[:5], None, *args[6:]) == fa2.FA2_ERR_INVALID_ARG          # dk null
     assert lib.fa2_bwd_dkdv(*args[:13], 0.0, *args[14:]) == fa2.FA2_ERR_INVALID_ARG         # scale
@@ -159,7 +161,7 @@ def varlen_fwd_args(**over):
 
 def varlen_bwd_args(**over):
     a = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, lse=FAKE, dout=FAKE, dq=FAKE, dk=FAKE, dv=FAKE, cu=FAKE, ws=FAKE,
-             ws_bytes=1024, B=3, T=100, H=2, d=64, scale=0.125, causal=1, wl=-1, wr=-1, alibi=None, stream=None)
+             ws_bytes=2048, B=3, T=100, H=2, d=64, scale=0.125, causal=1, wl=-1, wr=-1, alibi=None, stream=None)
     a.update(over)
     return [a[k] for k in ("q", "k", "v", "out", "lse", "dout", "dq", "dk", "dv", "cu", "ws", "ws_bytes", "B", "T",
                            "H", "d", "scale", "causal", "wl", "wr", "alibi", "stream")]
@@ -188,8 +190,8 @@ def test_varlen_entry_points_reject_bad_arguments(lib, over, status):
 
 def test_varlen_backward_checks_workspace_and_gradients(lib):
     need = fa2.fa2_bwd_workspace_size(1, 2, 100, 64)
-    assert need >= 2 * 100 * 4
-    assert lib.fa2_bwd_varlen(*varlen_bwd_args(ws_bytes=2 * 100 * 4 - 4)) == fa2.FA2_ERR_INVALID_ARG
+    assert need >= 2 * 1024  # -D and -LSE / scale: 2 * 100 floats each, rounded up to 256 bytes
+    assert lib.fa2_bwd_varlen(*varlen_bwd_args(ws_bytes=2 * 1024 - 4)) == fa2.FA2_ERR_INVALID_ARG
     assert lib.fa2_bwd_varlen(*varlen_bwd_args(dk=None)) == fa2.FA2_ERR_INVALID_ARG
     assert lib.fa2_bwd_varlen(*varlen_bwd_args(dout=MISALIGNED)) == fa2.FA2_ERR_INVALID_ARG
 
@@ -202,7 +204,7 @@ def test_varlen_empty_problem_is_ok_and_launches_nothing(lib, over):
 
 def sparse_args(fn, **over):
     a = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, lse=FAKE, dout=FAKE, dq=FAKE, dk=FAKE, dv=FAKE, ws=FAKE,
-             ws_bytes=4096, B=1, H=2, N=300, d=64, scale=0.125, causal=1, wl=-1, wr=-1, alibi=None, mask=FAKE,
+             ws_bytes=8192, B=1, H=2, N=300, d=64, scale=0.125, causal=1, wl=-1, wr=-1, alibi=None, mask=FAKE,
              sb=0, sh=9, stream=None)
     a.update(over)
     if fn == "fa2_fwd_blocksparse":
@@ -239,13 +241,13 @@ def test_blocksparse_empty_problem_is_ok(lib, fn):
 
 
 def test_blocksparse_backward_checks_workspace(lib):
-    args = sparse_args("fa2_bwd_blocksparse", ws_bytes=2 * 300 * 4 - 1)
+    args = sparse_args("fa2_bwd_blocksparse", ws_bytes=2 * 2560 - 1)
     assert lib.fa2_bwd_blocksparse(*args) == fa2.FA2_ERR_INVALID_ARG
 
 
 def dropout_args(fn, **over):
     a = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, lse=FAKE, dout=FAKE, dq=FAKE, dk=FAKE, dv=FAKE, ws=FAKE,
-             ws_bytes=4096, B=1, H=2, N=300, d=128, scale=0.125, causal=1, wl=-1, wr=-1, alibi=None, p=0.1,
+             ws_bytes=8192, B=1, H=2, N=300, d=128, scale=0.125, causal=1, wl=-1, wr=-1, alibi=None, p=0.1,
              seed=1, offset=2, stream=None)
     a.update(over)
     if fn == "fa2_fwd_dropout":
@@ -285,7 +287,7 @@ def test_dropout_empty_problem_is_ok(lib, fn):
 
 
 def test_dropout_backward_checks_workspace(lib):
-    args = dropout_args("fa2_bwd_dropout", ws_bytes=2 * 300 * 4 - 1)
+    args = dropout_args("fa2_bwd_dropout", ws_bytes=2 * 2560 - 1)
     assert lib.fa2_bwd_dropout(*args) == fa2.FA2_ERR_INVALID_ARG
 
 
@@ -297,12 +299,12 @@ def test_forward_rejects_too_many_heads_for_32_bit_tile_offsets(lib, fn):
 
 
 def test_workspace_size(lib):
-    # delta [B,H,N] + float32 dQ accumulator [B,H,N,d], each rounded up to 256 bytes
+    # -D and -LSE / scale [B,H,N] + float32 dQ accumulator [B,H,N,d], each rounded up to 256 bytes
     B, H, N, d = 4, 16, 4096, 128
     rows = B * H * N
     up = lambda x: (x + 255) // 256 * 256
-    assert fa2.fa2_bwd_workspace_size(B, H, N, d) == up(rows * d * 4) + up(rows * 4)
-    assert fa2.fa2_bwd_workspace_size(1, 1, 17, 64) == up(17 * 64 * 4) + up(17 * 4)
+    assert fa2.fa2_bwd_workspace_size(B, H, N, d) == up(rows * d * 4) + 2 * up(rows * 4)
+    assert fa2.fa2_bwd_workspace_size(1, 1, 17, 64) == up(17 * 64 * 4) + 2 * up(17 * 4)
     assert fa2.fa2_bwd_workspace_size(0, 1, 17, 64) == 0
     assert fa2.fa2_bwd_workspace_size(1, 1, 17, 96) == 0
 

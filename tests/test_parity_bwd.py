@@ -131,12 +131,12 @@ def test_pass_entry_points_match_fa2_bwd_on_two_streams(gpu_lib, d):
     scale = scale_of(d)
     out, lse = gpu_lib.flash_attn_fwd(dev["q"], dev["k"], dev["v"], scale, True, (200, 0), sl)
     ref = gpu_lib.flash_attn_bwd(dev["dout"], dev["q"], dev["k"], dev["v"], out, lse, scale, True, (200, 0), sl)
-    ws_bytes = (B * H * N * 4 + 255) // 256 * 256  # only D is needed by the passes
+    ws_bytes = 2 * ((B * H * N * 4 + 255) // 256 * 256)  # -D and -LSE / scale per row
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
     dq, dk, dv = (torch.empty_like(dev["q"]) for _ in range(3))
     s0 = torch.cuda.current_stream()
     s1 = torch.cuda.Stream()
-    gpu_lib.fa2_bwd_prep(out, dev["dout"], ws, ws_bytes, B, H, N, d, s0.cuda_stream)
+    gpu_lib.fa2_bwd_prep(out, dev["dout"], lse, ws, ws_bytes, B, H, N, d, scale, s0.cuda_stream)
     ev = torch.cuda.Event()
     ev.record(s0)
     s1.wait_event(ev)

@@ -68,7 +68,10 @@ struct BwdShape {
   static constexpr int CPR = D / 8;                     // 16-byte chunks per row
   static constexpr int KS = D / 16;                     // MFMA steps over d
   static constexpr int MB = D / 32;                     // 32-row blocks of d
-  static constexpr int K_BYTES = BK * D * 2;            // resident K tile
+  // Resident K tile. The split pass pads its rows by 16 bytes instead of swizzling
+  // them (it reads K only along rows); the atomic pass also reads it transposed.
+  static constexpr int KROWB = 2 * D + (DET_ ? 16 : 0);
+  static constexpr int K_BYTES = BK * KROWB;
   static constexpr int QT_BYTES = BQ * D * 2;           // one Q or dO tile
   static constexpr int STAGE_BYTES = 2 * QT_BYTES + 2 * BQ * 4;
   static constexpr int DS_BYTES = DET_ ? 0 : BK * BQ * 2;  // dS^T, [key][query]
@@ -206,9 +209,30 @@ __global__ __launch_bounds__(NW * 64, ((D == 128 && !DET) ? 4 : 8) / NW) void bw
 #pragma unroll
   for (int ks = 0; ks < S::KS; ++ks)
     vf[ks] = kj < N ? *reinterpret_cast<const bf16x8*>(vg + (int64_t)kj * rs + 16 * ks + 8 * hh) : bf16x8{};
+  // Resident K tile (B operand of S, and K of dQ = dS K). Split pass: padded rows
+  // (pitch 2d + 16 bytes), so that the reads of the d-steps differ by constant
+  // offsets and the 16-byte shift per row spreads one column over all banks; rows
+  // past the sequence repeat its last row.
+  constexpr int K_PER_T = S::BK * S::CPR / S::NT;  // 16-byte pieces per thread
+  bf16x8 kpiece[DET ? K_PER_T : 1];
+  if constexpr (DET) {
+#pragma unroll
+    for (int n = 0; n < K_PER_T; ++n) {
+      const int c = tid + n * S::NT, row = c / S::CPR;
+      const int key = min(k0 + row, N - 1);
+      kpiece[n] = *reinterpret_cast<const bf16x8*>(kg + (int64_t)key * rs + (c % S::CPR) * 8);
+    }
+  }
   wait_vm_all();
-  // Resident K tile (B operand of S, and K of dQ = dS K).
-  dma_tile<D, S::BK, NW>(k_lds, kg, rs, k0, N, w, lane);
+  if constexpr (DET) {
+#pragma unroll
+    for (int n = 0; n < K_PER_T; ++n) {
+      const int c = tid + n * S::NT;
+      *reinterpret_cast<bf16x8*>(k_lds + (c / S::CPR) * S::KROWB + (c % S::CPR) * 16) = kpiece[n];
+    }
+  } else {
+    dma_tile<D, S::BK, NW>(k_lds, kg, rs, k0, N, w, lane);
+  }
 
   const float slope2 = ALIBI ? p.alibi[h] * kLog2e : 0.f;
 
@@ -244,9 +268,20 @@ __global__ __launch_bounds__(NW * 64, ((D == 128 && !DET) ? 4 : 8) / NW) void bw
   // Per-lane LDS bases; every read below is base ^ constant or base + constant.
   const int ar = kperm(l32);  // A-operand row (query) for S and dP
   uint32_t qa_base = ar * ROWB + ((hh ^ tile_swz<D>(ar)) << 4);
-  // K rows of this wave's keys, as LDS addresses (K_OFF is a multiple of 256, so XOR
-  // with a chunk offset below 256 commutes with adding it).
-  uint32_t kb_base = S::K_OFF + (32 * w + l32) * ROWB + ((hh ^ tile_swz<D>(l32)) << 4);
+  // Its addresses for the d-steps, kept in registers across the loop (formed per
+  // block instead under dropout, whose generator needs the registers).
+  constexpr bool KEEP_QX = !DROPOUT;
+  uint32_t qx[S::KS];
+#pragma unroll
+  for (int ks = 0; ks < S::KS; ++ks) {
+    qx[ks] = qa_base ^ (ks << 5);
+    if (KEEP_QX) opaque(qx[ks]);
+  }
+  // K rows of this wave's keys, as LDS addresses: padded rows (split pass), or
+  // swizzled ones (K_OFF is a multiple of 256, so XOR with a chunk offset below 256
+  // commutes with adding it).
+  uint32_t kb_base = DET ? S::K_OFF + (32 * w + l32) * S::KROWB + (hh << 4)
+                         : S::K_OFF + (32 * w + l32) * ROWB + ((hh ^ tile_swz<D>(l32)) << 4);
   const int tr0 = 8 * hh + (j >> 2);
   const int c0 = 2 * (g & 1) + ((j & 3) >> 1);
   uint32_t tr_lo = tr0 * ROWB + ((c0 ^ tile_swz<D>(tr0)) << 4) + (j & 1) * 8;
@@ -319,7 +354,11 @@ __global__ __launch_bounds__(NW * 64, ((D == 128 && !DET) ? 4 : 8) / NW) void bw
     constexpr int stg = decltype(stage_c)::value;
     if (u + NST - 1 < n_tiles)
       issue_q((int)(entry_at(u + NST - 1) & kTileIndexMask), std::integral_constant<int, (stg + NST - 1) % NST>{});
-    opaque(qa_base);
+    if (!KEEP_QX) {
+      opaque(qa_base);
+#pragma unroll
+      for (int ks = 0; ks < S::KS; ++ks) qx[ks] = qa_base ^ (ks << 5);
+    }
     opaque(kb_base);
     opaque(tr_lo);
     opaque(tr_hi);
@@ -338,9 +377,6 @@ __global__ __launch_bounds__(NW * 64, ((D == 128 && !DET) ? 4 : 8) / NW) void bw
       const float* sinit_t = reinterpret_cast<const float*>(q_t + 2 * S::QT_BYTES);  // -LSE / scale
       const float* ndel_t = sinit_t + S::BQ;                                           // -D
 
-      uint32_t qx[S::KS];
-#pragma unroll
-      for (int ks = 0; ks < S::KS; ++ks) qx[ks] = qa_base ^ (ks << 5);
       // S - LSE / scale = Q K^T - LSE / scale: rows are queries (A lane m reads row
       // kperm(m)), columns are this wave's keys; register r holds query key_of_reg(r, hh).
       f32x16 s;
@@ -349,7 +385,7 @@ __global__ __launch_bounds__(NW * 64, ((D == 128 && !DET) ? 4 : 8) / NW) void bw
 #pragma unroll
       for (int ks = 0; ks < S::KS; ++ks) {
         const bf16x8 a = lds_read16_at(kQ + qx[ks]);
-        const bf16x8 bk = lds_read16_at(kb_base ^ (ks << 5));
+        const bf16x8 bk = lds_read16_at(DET ? kb_base + (ks << 5) : kb_base ^ (ks << 5));
         s = mfma32(a, bk, s);
       }
       // Masks. Dense and packed batches mask S in place (-inf for hidden keys), a branch
@@ -558,6 +594,11 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq_det_kernel(BwdParams p
   const float lse_qi = qi < N ? p.lse[stat0 + qi] : -INFINITY;
   const float lse2 = lse_qi > -INFINITY ? lse_qi * kLog2e : INFINITY;
   const float ndelta = qi < N ? p.ndelta[stat0 + qi] : 0.f;  // -D
+  // dP^T accumulators start at -D (every register of a lane holds this lane's query),
+  // so that the MFMAs hand back dP - D; under dropout they start at 0.
+  f32x16 dp_init;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) dp_init[r] = DROPOUT ? 0.f : ndelta;
   const float slope2 = ALIBI ? p.alibi[h] * kLog2e : 0.f;
 
   int kv_lo = 0, kv_hi = N;
@@ -635,7 +676,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq_det_kernel(BwdParams p
       constexpr uint32_t kK = st * STAGE, kV = kK + TILE;
       // S^T = K Q^T and dP^T = V dO^T: rows are keys (A lane m reads row kperm(m)), columns queries.
       // The K and V fragments of step ks + 1 are read while the MFMAs of step ks run.
-      f32x16 s = f32x16{}, dp = f32x16{};
+      f32x16 s = f32x16{}, dp = dp_init;
       bf16x8 kv[2][2];
       auto kvload = [&](int ks, bf16x8(&dst)[2]) __attribute__((always_inline)) {
         const uint32_t ax = abase ^ (ks << 5);
@@ -709,8 +750,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq_det_kernel(BwdParams p
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int r = 8 * kk + e;
-          const float dpr = DROPOUT ? (((keep >> r) & 1u) ? dp[r] * p.drop_scale : 0.f) : dp[r];
-          d8[e] = pr[r] * (dpr + ndelta);
+          d8[e] = DROPOUT ? pr[r] * ((((keep >> r) & 1u) ? dp[r] * p.drop_scale : 0.f) + ndelta) : pr[r] * dp[r];
         }
         const bf16x8 dsb = pack_bf16x8(d8[0], d8[1], d8[2], d8[3], d8[4], d8[5], d8[6], d8[7]);
 #pragma unroll

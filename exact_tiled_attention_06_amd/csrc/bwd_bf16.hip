@@ -788,10 +788,10 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq_det_kernel(BwdParams p
 
 // ---------------------------------------------------------------- launch
 #ifndef FA2_BWD_NW
-#define FA2_BWD_NW 8
+#define FA2_BWD_NW 4
 #endif
 #ifndef FA2_BWD_NST
-#define FA2_BWD_NST 4
+#define FA2_BWD_NST 2
 #endif
 #ifndef FA2_DQ_NW
 #define FA2_DQ_NW 4
@@ -819,7 +819,10 @@ static hipError_t launch_prep_d(const BwdParams& p, bool zero_acc, hipStream_t s
 // Pass 2: the key-block pass (dK, dV; with DET = false also the atomic dQ).
 template <int D, bool ALIBI, bool DET, bool VARLEN, bool SPARSE, bool DROPOUT = false>
 static hipError_t launch_main_d(const BwdParams& p0, hipStream_t stream) {
-  // Split dQ pass (DET): deeper Q/dO ring and 8 waves per key block; atomic dQ:
+  // Split dQ pass (DET): 4 waves per 128-key block, two workgroups per CU (2-stage
+  // rings at d = 128, so that both fit in LDS). Each workgroup has its own barriers,
+  // so the two drift out of step and one's softmax runs beside the other's MFMAs;
+  // one 8-wave workgroup with a 4-stage ring measured 3-4 % slower. Atomic dQ:
   // 4 waves, 2 stages (its dS^T buffer and dQ step need the room).
   constexpr int NW = DET ? (D == 128 ? FA2_BWD_NW : 4) : 4;
   constexpr int NST = DET ? (D == 128 ? FA2_BWD_NST : 3) : 2;

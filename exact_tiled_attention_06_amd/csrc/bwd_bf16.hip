@@ -548,7 +548,7 @@ __global__ __launch_bounds__(NW * 64, ((D == 128 && !DET) ? 4 : 8) / NW) void bw
 // scalars, and dS^T feeds dQ^T += K^T dS^T as the B operand straight from
 // registers (K^T read transposed from the K tile).
 template <int D, bool ALIBI, int NW, int NST, bool VARLEN, bool SPARSE, bool DROPOUT>
-__global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq_det_kernel(BwdParams p) {
+__global__ __launch_bounds__(NW * 64, 2) void bwd_dq_det_kernel(BwdParams p) {  // 2 waves per SIMD
   static_assert(!(VARLEN && SPARSE), "packed batches have no block mask");
   static_assert(!DROPOUT || !(VARLEN || SPARSE), "dropout runs on fixed-length dense batches");
   static_assert(!SPARSE || NW * 32 == kSparseBlock, "a workgroup covers one mask row");
@@ -842,7 +842,7 @@ static hipError_t launch_main_d(const BwdParams& p0, hipStream_t stream) {
 // Pass 3 of the split backward: dQ by a sweep over key tiles per query block.
 template <int D, bool ALIBI, bool VARLEN, bool SPARSE, bool DROPOUT>
 static hipError_t launch_dq_d(const BwdParams& p0, hipStream_t stream) {
-  constexpr int DNW = D == 128 ? FA2_DQ_NW : 4;
+  constexpr int DNW = (D == 128 && !SPARSE) ? FA2_DQ_NW : 4;  // block-sparse: one mask row per workgroup
   constexpr int DNST = FA2_DQ_NST;
   auto kdq = bwd_dq_det_kernel<D, ALIBI, DNW, DNST, VARLEN, SPARSE, DROPOUT>;
   constexpr int DQ_LDS = DNST * 2 * 32 * D * 2 + (SPARSE ? 2 * (kSparseMaxN / 32) : 0);  // ring (+ tile list)

@@ -633,6 +633,15 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_det_kernel(BwdParams p) {  
   }
   const int kr = kperm(l32);
   uint32_t abase = kr * ROWB + ((hh ^ tile_swz<D>(kr)) << 4);  // K, V rows (A operands)
+  // Its addresses for the d-steps, kept in registers across the loop (formed per
+  // tile instead under dropout, whose generator needs the registers).
+  constexpr bool KEEP_AX = !DROPOUT;
+  uint32_t ax[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    ax[ks] = abase ^ (ks << 5);
+    if (KEEP_AX) opaque(ax[ks]);
+  }
   const int tr0 = 8 * hh + (j >> 2);
   const int c0 = 2 * (g & 1) + ((j & 3) >> 1);
   uint32_t tr_lo = tr0 * ROWB + ((c0 ^ tile_swz<D>(tr0)) << 4) + (j & 1) * 8;
@@ -665,7 +674,11 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_det_kernel(BwdParams p) {  
     constexpr int st = decltype(stage_c)::value;
     if (u + NST - 1 < n_tiles) issue(tile_at(u + NST - 1), std::integral_constant<int, (st + NST - 1) % NST>{});
     const int t = tile_at(u);
-    opaque(abase);
+    if (!KEEP_AX) {
+      opaque(abase);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) ax[ks] = abase ^ (ks << 5);
+    }
     opaque(tr_lo);
     opaque(tr_hi);
     const int j0 = t * BC, j1 = j0 + BC - 1;
@@ -679,9 +692,8 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_det_kernel(BwdParams p) {  
       f32x16 s = f32x16{}, dp = dp_init;
       bf16x8 kv[2][2];
       auto kvload = [&](int ks, bf16x8(&dst)[2]) __attribute__((always_inline)) {
-        const uint32_t ax = abase ^ (ks << 5);
-        dst[0] = lds_read16_at(kK + ax);
-        dst[1] = lds_read16_at(kV + ax);
+        dst[0] = lds_read16_at(kK + ax[ks]);
+        dst[1] = lds_read16_at(kV + ax[ks]);
       };
       kvload(0, kv[0]);
       static_for<0, KS>([&](auto kc) {

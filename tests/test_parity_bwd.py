@@ -147,3 +147,26 @@ def test_pass_entry_points_match_fa2_bwd_on_two_streams(gpu_lib, d):
     torch.cuda.synchronize()
     for x, y in zip((dq, dk, dv), ref):
         assert torch.equal(x, y)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_prep_pass_writes_minus_d_and_minus_lse_over_scale(gpu_lib, d):
+    """fa2_bwd_prep's workspace: -D per row (D = rowsum(dO * O), fp64 from the given O
+    and dO) at offset 0, then -LSE / scale per row, each array rounded up to 256 bytes."""
+    B, H, N = 2, 3, 77
+    cpu, dev, _ = gpu_inputs(B, H, N, d, "bf16", seed=45, with_dout=True)
+    scale = scale_of(d)
+    out, lse = gpu_lib.flash_attn_fwd(dev["q"], dev["k"], dev["v"], scale, True, (-1, -1), None)
+    rows = B * H * N
+    part = (rows * 4 + 255) // 256 * 256
+    ws = torch.full((2 * part,), 0xFF, dtype=torch.uint8, device="cuda")
+    gpu_lib.fa2_bwd_prep(out, dev["dout"], lse, ws, 2 * part, B, H, N, d, scale, None)
+    torch.cuda.synchronize()
+    nd = ws[:rows * 4].view(torch.float32).cpu().numpy().reshape(B, H, N)
+    si = ws[part:part + rows * 4].view(torch.float32).cpu().numpy().reshape(B, H, N)
+    o = to_np(out).astype(np.float64)
+    do = cpu["dout"].double().numpy()
+    d_ref = np.einsum("bnhd,bnhd->bhn", o, do)
+    assert np.max(np.abs(nd + d_ref)) <= 1e-4 * max(1.0, np.max(np.abs(d_ref)))
+    lse_np = lse.cpu().numpy().astype(np.float64)
+    np.testing.assert_allclose(si, -lse_np / scale, rtol=1e-6, atol=1e-6)

@@ -296,6 +296,18 @@ def flash_attn_fwd(q, k, v, softmax_scale=None, causal=False, window_size=(-1, -
     return out, lse
 
 
+def _split_workspace_bytes(rows):
+    """Workspace of the atomic-free backward: -D and -LSE / scale, one float32 each per
+    row, each array rounded up to 256 bytes (include/fa2.h)."""
+    return max(2 * ((4 * rows + 255) // 256 * 256), 256)
+
+
+def _atomic_dq_selected(deterministic):
+    """fa2_bwd accumulates dQ atomically only when asked for no determinism and
+    FA2_BWD_ATOMIC_DQ=1 is set; only that variant needs the float32 dQ accumulator."""
+    return not deterministic and os.environ.get("FA2_BWD_ATOMIC_DQ") == "1"
+
+
 def flash_attn_bwd(dout, q, k, v, out, lse, softmax_scale=None, causal=False, window_size=(-1, -1),
                    alibi_slopes=None, deterministic=False, workspace=None, dropout_p=0.0, seed=0, offset=0):
     """Exact attention backward from the forward's out and lse. bf16 [B, N, H, d] tensors.
@@ -307,9 +319,10 @@ def flash_attn_bwd(dout, q, k, v, out, lse, softmax_scale=None, causal=False, wi
     B, N, H, d = q.shape
     scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    need = fa2_bwd_workspace_size(B, H, N, d)
     if workspace is None:
-        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+        need = (fa2_bwd_workspace_size(B, H, N, d) if _atomic_dq_selected(deterministic) and not dropout_p
+                else _split_workspace_bytes(B * H * N))
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     sl = _slopes(alibi_slopes, H, q.device)
     if dropout_p:
         fa2_bwd_dropout(q, k, v, out, lse, dout, dq, dk, dv, workspace, workspace.numel() * workspace.element_size(),
@@ -360,7 +373,7 @@ def flash_attn_varlen_bwd(dout, q, k, v, out, lse, cu_seqlens, softmax_scale=Non
     scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     if workspace is None:
-        workspace = torch.empty(max(fa2_bwd_workspace_size(1, H, T, d), 256), dtype=torch.uint8, device=q.device)
+        workspace = torch.empty(_split_workspace_bytes(H * T), dtype=torch.uint8, device=q.device)
     fa2_bwd_varlen(q, k, v, out, lse, dout, dq, dk, dv, cu, workspace, workspace.numel() * workspace.element_size(),
                    cu.numel() - 1, T, H, d, scale, int(bool(causal)), window_size[0], window_size[1],
                    _slopes(alibi_slopes, H, q.device))
@@ -414,7 +427,7 @@ def flash_attn_blocksparse_bwd(dout, q, k, v, out, lse, block_mask, softmax_scal
     scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     if workspace is None:
-        workspace = torch.empty(max(fa2_bwd_workspace_size(B, H, N, d), 256), dtype=torch.uint8, device=q.device)
+        workspace = torch.empty(_split_workspace_bytes(B * H * N), dtype=torch.uint8, device=q.device)
     fa2_bwd_blocksparse(q, k, v, out, lse, dout, dq, dk, dv, workspace, workspace.numel() * workspace.element_size(),
                         B, H, N, d, scale, int(bool(causal)), window_size[0], window_size[1],
                         _slopes(alibi_slopes, H, q.device), m, sb, sh)

@@ -321,3 +321,15 @@ def test_product_package_does_not_touch_the_oracle():
             if f.endswith((".py", ".hip", ".hpp", ".cpp", ".h")):
                 text = open(os.path.join(dirpath, f), encoding="utf-8").read()
                 assert "oracle" not in text.lower().replace("no oracle", ""), f
+
+
+def test_wrapper_workspace_for_the_atomic_free_backward(lib, monkeypatch):
+    # -D and -LSE / scale only: the library's size minus the float32 dQ accumulator
+    up = lambda x: (x + 255) // 256 * 256
+    for B, H, N, d in [(4, 32, 8192, 128), (1, 3, 77, 64), (2, 1, 1, 128)]:
+        rows = B * H * N
+        assert fa2._split_workspace_bytes(rows) == fa2.fa2_bwd_workspace_size(B, H, N, d) - up(rows * d * 4)
+    monkeypatch.delenv("FA2_BWD_ATOMIC_DQ", raising=False)
+    assert not fa2._atomic_dq_selected(False)
+    monkeypatch.setenv("FA2_BWD_ATOMIC_DQ", "1")
+    assert fa2._atomic_dq_selected(False) and not fa2._atomic_dq_selected(True)

@@ -99,7 +99,7 @@ def test_dv_columns_sum_to_dout_columns(gpu_lib):
 
 
 @pytest.mark.parametrize("deterministic", [False, "atomic"])
-@pytest.mark.parametrize("number", [4, 5])
+@pytest.mark.parametrize("number", [2, 3, 4, 5])
 def test_full_size_workload_sampled_rows(gpu_lib, number, deterministic):
     w = workloads.WORKLOADS[number]
     say(f"bwd full-size {w.describe()} det={deterministic}")

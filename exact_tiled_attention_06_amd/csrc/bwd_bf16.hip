@@ -805,6 +805,12 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_det_kernel(BwdParams p) {  
 #ifndef FA2_BWD_NST
 #define FA2_BWD_NST 2
 #endif
+#ifndef FA2_BWD64_NST
+#define FA2_BWD64_NST 3
+#endif
+#ifndef FA2_DQ64_NST
+#define FA2_DQ64_NST 3
+#endif
 #ifndef FA2_DQ_NW
 #define FA2_DQ_NW 4
 #endif
@@ -837,7 +843,7 @@ static hipError_t launch_main_d(const BwdParams& p0, hipStream_t stream) {
   // one 8-wave workgroup with a 4-stage ring measured 3-4 % slower. Atomic dQ:
   // 4 waves, 2 stages (its dS^T buffer and dQ step need the room).
   constexpr int NW = DET ? (D == 128 ? FA2_BWD_NW : 4) : 4;
-  constexpr int NST = DET ? (D == 128 ? FA2_BWD_NST : 3) : 2;
+  constexpr int NST = DET ? (D == 128 ? FA2_BWD_NST : FA2_BWD64_NST) : 2;
   using S = BwdShape<D, NW, NST, DET>;
   auto kmain = bwd_main_kernel<D, ALIBI, DET, NW, NST, VARLEN, SPARSE, DROPOUT>;
   // + the query-tile list (SPARSE) or 32 keep-mask words per wave (DROPOUT)
@@ -855,7 +861,7 @@ static hipError_t launch_main_d(const BwdParams& p0, hipStream_t stream) {
 template <int D, bool ALIBI, bool VARLEN, bool SPARSE, bool DROPOUT>
 static hipError_t launch_dq_d(const BwdParams& p0, hipStream_t stream) {
   constexpr int DNW = (D == 128 && !SPARSE) ? FA2_DQ_NW : 4;  // block-sparse: one mask row per workgroup
-  constexpr int DNST = FA2_DQ_NST;
+  constexpr int DNST = D == 128 ? FA2_DQ_NST : FA2_DQ64_NST;
   auto kdq = bwd_dq_det_kernel<D, ALIBI, DNW, DNST, VARLEN, SPARSE, DROPOUT>;
   constexpr int DQ_LDS = DNST * 2 * 32 * D * 2 + (SPARSE ? 2 * (kSparseMaxN / 32) : 0);  // ring (+ tile list)
   static const hipError_t attr = set_lds(kdq, DQ_LDS);  // once per kernel; thread-safe initialisation

@@ -429,12 +429,15 @@ static hipError_t launch_fwd_cfg(const FwdParams& p0, hipStream_t stream) {
 #define FA2_FWD_NST 2
 #endif
 
+#ifndef FA2_FWD64_BC
+#define FA2_FWD64_BC 64
+#endif
 #ifndef FA2_FWD_BC
 #define FA2_FWD_BC 32
 #endif
 template <int D, bool VARLEN, bool SPARSE, bool DROPOUT>
 static hipError_t launch_fwd_d(const FwdParams& p, hipStream_t stream) {
-  constexpr int NW = SPARSE ? kSparseBlock / 32 : FA2_FWD_NW, NST = FA2_FWD_NST, BC = D == 128 ? FA2_FWD_BC : 64;
+  constexpr int NW = SPARSE ? kSparseBlock / 32 : FA2_FWD_NW, NST = FA2_FWD_NST, BC = D == 128 ? FA2_FWD_BC : FA2_FWD64_BC;
   return p.alibi != nullptr ? launch_fwd_cfg<D, NW, BC, NST, true, VARLEN, SPARSE, DROPOUT>(p, stream)
                             : launch_fwd_cfg<D, NW, BC, NST, false, VARLEN, SPARSE, DROPOUT>(p, stream);
 }

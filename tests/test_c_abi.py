@@ -1,0 +1,30 @@
+"""The C ABI from a C program: tests/c/abi_check.c, compiled as C99 by the host C
+compiler against include/fa2.h and linked with libfa2.so by name. Every call in it is
+rejected by argument validation or is an empty problem, both of which return before
+any HIP call, so it runs without a GPU and launches nothing."""
+import os
+import shutil
+import subprocess
+
+import pytest
+
+import exact_tiled_attention_06_amd as fa2
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_c_program_compiles_links_and_sees_the_documented_status_codes(tmp_path):
+    if not os.path.exists(fa2.LIB_PATH):
+        pytest.fail("libfa2.so is not built; run __graft_entry__.build()")
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no host C compiler")
+    libdir = os.path.dirname(fa2.LIB_PATH)
+    exe = str(tmp_path / "abi_check")
+    build = subprocess.run([cc, "-std=c99", "-Wall", "-Wextra", "-Werror", "-I", os.path.join(ROOT, "include"),
+                            os.path.join(ROOT, "tests", "c", "abi_check.c"), "-L", libdir, "-l:libfa2.so",
+                            f"-Wl,-rpath,{libdir}", "-o", exe], capture_output=True, text=True, timeout=120)
+    assert build.returncode == 0, build.stderr
+    run = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    assert run.returncode == 0, run.stdout + run.stderr
+    assert "0 failure(s)" in run.stdout

@@ -139,3 +139,46 @@ def test_explicit_stream(gpu_lib):
     s.synchronize()
     o_ref, _ = oracle.attention_forward(cpu["q"], cpu["k"], cpu["v"], 0.125)
     assert max_abs(to_np(out), o_ref) <= TOL_O_BF16
+
+
+def bf16_ulp(x):
+    """Spacing of bf16 numbers at |x| (8 significant bits): 2^(floor(log2|x|) - 7)."""
+    a = np.maximum(np.abs(np.asarray(x, dtype=np.float64)), np.finfo(np.float32).tiny)
+    return np.exp2(np.floor(np.log2(a)) - 7)
+
+
+@pytest.mark.parametrize("d,causal,window,alibi", [(128, True, (-1, -1), False), (64, False, (40, 9), True),
+                                                     (128, False, (-1, -1), False)])
+def test_error_within_the_bf16_rounding_bound(gpu_lib, d, causal, window, alibi):
+    """Every O element against a bound derived from the arithmetic rather than a flat
+    tolerance: the kernel rounds each weight P_ij to bf16 before P.V (relative error at
+    most 2^-8) and rounds O to bf16 once (half a bf16 ulp), so
+      |O_gpu - O| <= ulp(O) / 2 + 2^-8 * sum_j P_ij |v_j| + 1e-5
+    (fp32 accumulation and the exponential add far less than the slack). The
+    distribution of the error against |O| is printed."""
+    B, H, N = 1, 2, 700
+    cpu, dev, slopes = gpu_inputs(B, H, N, d, "bf16", seed=77 + d, alibi=alibi)
+    sc = scale_of(d)
+    out, lse = run_fwd(gpu_lib, dev, slopes, sc, causal, window)
+    q, k, v = (cpu[n].double().numpy() for n in ("q", "k", "v"))
+    o_gpu = to_np(out).astype(np.float64)
+    sl = None if slopes is None else slopes.numpy()
+    worst = 0.0
+    hist = np.zeros(4)
+    for h in range(H):
+        s = oracle.logits(q[0, :, h, :], k[0, :, h, :], np.arange(N), sc, causal, window[0], window[1],
+                          None if sl is None else float(sl[h]))
+        pm, _ = oracle.softmax_rows(s)
+        o_ref = pm @ v[0, :, h, :]
+        err = np.abs(o_gpu[0, :, h, :] - o_ref)
+        bound = 0.5 * np.maximum(bf16_ulp(o_ref), bf16_ulp(o_gpu[0, :, h, :])) + 2.0 ** -8 * (pm @ np.abs(v[0, :, h, :])) + 1e-5
+        worst = max(worst, float(np.max(err / bound)))
+        mag = np.abs(o_ref)
+        for i, (lo, hi) in enumerate([(0, 0.25), (0.25, 1), (1, 4), (4, np.inf)]):
+            sel = (mag >= lo) & (mag < hi)
+            if sel.any():
+                hist[i] = max(hist[i], float(err[sel].max()))
+    say(f"  max err by |O| in [0,.25) [.25,1) [1,4) [4,inf): {hist[0]:.2e} {hist[1]:.2e} {hist[2]:.2e} {hist[3]:.2e}; "
+        f"worst err/bound {worst:.3f}")
+    assert worst <= 1.0
+    assert np.max(hist) <= TOL_O_BF16

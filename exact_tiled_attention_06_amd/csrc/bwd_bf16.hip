@@ -18,7 +18,9 @@
 //     the parallelisation over blocks within one head of the FlashAttention-2
 //     paper abstract, item (2), applied to the key axis. Every wavefront owns
 //     32 keys and keeps its dK^T and dV^T accumulators in registers while the
-//     visible 32-query blocks stream through a 2-stage LDS ring.
+//     visible 32-query blocks stream through a 2-stage LDS ring; the block's K
+//     stays in LDS (rows padded by 16 bytes in the split pass, swizzled in the
+//     atomic one, which also reads it transposed).
 //     S = Q K^T and dP = dO V^T are computed with queries on the MFMA rows and
 //     the wave's keys on the columns, so P and dS come out of the C registers
 //     with eight consecutive queries per lane half: exactly the B operand of
@@ -36,8 +38,9 @@
 // SPARSE (128 x 128 block mask, deterministic variant only): each workgroup
 // compacts the tiles of its active blocks into an LDS list and streams only
 // those. In the key-block pass a list entry also carries which of the
-// workgroup's (up to two) key blocks are active for that query tile, and a
-// wave whose key block is off skips the tile's compute.
+// workgroup's key blocks are active for that query tile (one at the default
+// 128 keys per workgroup, up to two at 256), and a wave whose key block is
+// off skips the tile's compute.
 // DROPOUT (deterministic variant, fixed-length dense batches): the keep
 // matrix of the forward is regenerated from the same Philox4x64-10 counters.
 // With Z the keep matrix and r = 1 / (1 - p): dV = (P * Z)^T dO r,

@@ -356,6 +356,23 @@ constexpr uint64_t kPhiloxW1 = 0xBB67AE8584CAA73Bull;
 
 // Ten rounds; each multiplies two counter words into 128-bit products and
 // mixes the halves with the other two words and the key.
+// The 128-bit product a * M of a 64-bit value and a constant, as its low and
+// high 64-bit halves, from four 32 x 32 -> 64-bit multiply-adds: with
+// a = a1 2^32 + a0 and M = m1 2^32 + m0,
+//   p00 = a0 m0,  p01 = a0 m1 + hi32(p00),  p10 = a1 m0 + lo32(p01),
+//   lo = lo32(p10) 2^32 + lo32(p00),  hi = a1 m1 + hi32(p01) + hi32(p10),
+// where no step overflows 64 bits ((2^32 - 1)^2 + 2 (2^32 - 1) < 2^64).
+template <uint64_t M>
+__device__ __forceinline__ void mulhilo64(uint64_t a, uint64_t& lo, uint64_t& hi) {
+  constexpr uint32_t m0 = (uint32_t)M, m1 = (uint32_t)(M >> 32);
+  const uint32_t a0 = (uint32_t)a, a1 = (uint32_t)(a >> 32);
+  const uint64_t p00 = (uint64_t)a0 * m0;
+  const uint64_t p01 = (uint64_t)a0 * m1 + (p00 >> 32);
+  const uint64_t p10 = (uint64_t)a1 * m0 + (uint32_t)p01;
+  hi = (uint64_t)a1 * m1 + ((p01 >> 32) + (p10 >> 32));
+  lo = (p10 << 32) | (uint32_t)p00;
+}
+
 __device__ __forceinline__ void philox4x64_10(uint64_t c0, uint64_t c1, uint64_t c2, uint64_t c3, uint64_t k0,
                                               uint64_t k1, uint32_t (&out)[8]) {
 #pragma unroll
@@ -364,8 +381,9 @@ __device__ __forceinline__ void philox4x64_10(uint64_t c0, uint64_t c1, uint64_t
       k0 += kPhiloxW0;
       k1 += kPhiloxW1;
     }
-    const uint64_t lo0 = kPhiloxM0 * c0, hi0 = __umul64hi(kPhiloxM0, c0);
-    const uint64_t lo1 = kPhiloxM1 * c2, hi1 = __umul64hi(kPhiloxM1, c2);
+    uint64_t lo0, hi0, lo1, hi1;
+    mulhilo64<kPhiloxM0>(c0, lo0, hi0);
+    mulhilo64<kPhiloxM1>(c2, lo1, hi1);
     const uint64_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
     c0 = n0;
     c1 = lo1;

@@ -98,7 +98,8 @@ size_t fa2_bwd_workspace_size(int B, int H, int N, int d);
  * as written by fa2_fwd with the same arguments); dq, dk, dv: bf16 [B, N, H, d]
  * (written). workspace: device memory (see fa2_bwd_workspace_size;
  * workspace_bytes says how much was given; too little is FA2_ERR_INVALID_ARG);
- * its contents need not be initialised and are overwritten. deterministic != 0 guarantees bitwise-repeatable results: dQ is
+ * its contents need not be initialised and are overwritten.
+ * deterministic != 0 guarantees bitwise-repeatable results: dQ is
  * formed by a separate pass over query blocks, without atomics. With
  * deterministic = 0 the library may choose; it currently uses the same pass
  * (the faster one on MI355X). Setting the environment variable
@@ -116,7 +117,8 @@ fa2_status_t fa2_bwd(const void* q, const void* k, const void* v, const void* ou
 /*
  * The three passes of fa2_bwd's default (atomic-free) algorithm as separate
  * calls, for callers that schedule them themselves (for instance the dK/dV
- * and dQ passes on two streams: both depend only on fa2_bwd_prep). Arguments
+ * and dQ passes on two streams: both depend only on fa2_bwd_prep; on MI355X
+ * the two in order on one stream measured faster). Arguments
  * mean what they mean for fa2_bwd; the same workspace (at least
  * 2 * round_up(4 * B * H * N, 256) bytes) must be passed to all three, with the
  * same lse and softmax_scale, and fa2_bwd_prep must have completed before the

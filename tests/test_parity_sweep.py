@@ -18,7 +18,7 @@ from parity_utils import TOL_GRAD_REL, TOL_LSE, TOL_O_BF16, max_abs, rel_to_max,
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 32
+N_CASES = 64
 
 
 def draw(case):
@@ -105,7 +105,7 @@ def draw_packed(case):
     return lengths, H, d, causal, (wl, wr), bool(r.integers(0, 2))
 
 
-@pytest.mark.parametrize("case", range(12))
+@pytest.mark.parametrize("case", range(24))
 def test_seeded_packed_sweep(gpu_lib, case):
     fa2 = gpu_lib
     lengths, H, d, causal, window, alibi = draw_packed(case)
@@ -150,7 +150,7 @@ def draw_sparse(case):
     return B, H, N, d, causal, window, bool(r.integers(0, 2)), density, shared
 
 
-@pytest.mark.parametrize("case", range(12))
+@pytest.mark.parametrize("case", range(24))
 def test_seeded_blocksparse_sweep(gpu_lib, case):
     fa2 = gpu_lib
     B, H, N, d, causal, window, alibi, density, shared = draw_sparse(case)

@@ -221,9 +221,10 @@ void fwd_bf16_kernel(FwdParams p) {
     constexpr int st = decltype(stage_c)::value;
     if (u + NST - 1 < n_tiles) issue(tile_at(u + NST - 1), std::integral_constant<int, (st + NST - 1) % NST>{});
     const int t = tile_at(u);
-    opaque(kbase);
-    opaque(vbase_lo);
-    opaque(vbase_hi);
+    // The read addresses of the d-steps and d-blocks (base ^ constant) stay in
+    // registers across the loop; under ALiBi the K addresses are formed per tile,
+    // as its bias terms need the registers.
+    if (ALIBI) opaque(kbase);
     const int j0 = t * BC;
     const int j1 = j0 + BC - 1;
     const bool skip = !wave_live || (p.wr >= 0 && j0 > wq_last + p.wr) || (p.wl >= 0 && j1 < qw0 - p.wl);

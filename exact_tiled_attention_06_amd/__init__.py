@@ -30,7 +30,7 @@ import os
 __all__ = [
     "FA2Error", "LIB_PATH", "load_library", "fa2_fwd", "fa2_fwd_f32", "fa2_bwd",
     "fa2_bwd_workspace_size", "fa2_bwd_prep", "fa2_bwd_dkdv", "fa2_bwd_dq", "fa2_fwd_varlen", "fa2_bwd_varlen",
-    "fa2_fwd_blocksparse", "fa2_bwd_blocksparse", "fa2_fwd_dropout", "fa2_bwd_dropout", "fa2_status_string", "fa2_version", "flash_attn_fwd",
+    "fa2_fwd_blocksparse", "fa2_bwd_blocksparse", "fa2_fwd_dropout", "fa2_bwd_dropout", "fa2_status_string", "fa2_version", "fa2_effective_window", "flash_attn_fwd",
     "flash_attn_bwd", "flash_attn_varlen_fwd", "flash_attn_varlen_bwd", "flash_attn_blocksparse_fwd",
     "flash_attn_blocksparse_bwd", "BLOCKSPARSE_BLOCK", "FA2_OK", "FA2_ERR_INVALID_ARG", "FA2_ERR_UNSUPPORTED", "FA2_ERR_HIP",
 ]
@@ -73,6 +73,7 @@ SIGNATURES = {
                          _P, _F, _U64, _U64, _P], _I),
     "fa2_status_string": ([_I], ctypes.c_char_p),
     "fa2_version": ([], _I),
+    "fa2_effective_window": ([_I, _I, _I, _I, ctypes.POINTER(_I), ctypes.POINTER(_I)], _I),
 }
 
 
@@ -129,6 +130,15 @@ def fa2_status_string(status: int) -> str:
 
 def fa2_version() -> int:
     return int(load_library().fa2_version())
+
+
+def fa2_effective_window(n, causal, window_left, window_right):
+    """(left, right) window the library applies for n tokens (host-only, no GPU)."""
+    left, right = _I(0), _I(0)
+    st = load_library().fa2_effective_window(int(n), int(causal), int(window_left), int(window_right),
+                                             ctypes.byref(left), ctypes.byref(right))
+    _check(st, "fa2_effective_window")
+    return left.value, right.value
 
 
 def fa2_fwd(q, k, v, out, lse, B, H, N, d, softmax_scale, causal, window_left, window_right,
@@ -257,6 +267,22 @@ def _check_tensors(*ts):
             raise FA2Error("q, k, v (and out, dout) must share dtype and shape")
 
 
+def _check_aux(lse, shape, device, workspace=None):
+    """The forward's lse (float32, contiguous, the given shape, on the tensors' GPU)
+    and, if given, a caller's workspace (on the same GPU): the kernels index them
+    by position, so a wrong layout would read the wrong rows."""
+    import torch
+    if not isinstance(lse, torch.Tensor) or lse.dtype != torch.float32:
+        raise FA2Error("lse must be a float32 tensor (the forward's output)")
+    if tuple(lse.shape) != tuple(shape) or not lse.is_contiguous():
+        raise FA2Error(f"lse must be contiguous with shape {tuple(shape)}, got {tuple(lse.shape)}")
+    if lse.device != device:
+        raise FA2Error("lse must be on the tensors' GPU")
+    if workspace is not None:
+        if not isinstance(workspace, torch.Tensor) or workspace.device != device or not workspace.is_contiguous():
+            raise FA2Error("workspace must be a contiguous tensor on the tensors' GPU")
+
+
 def _slopes(alibi_slopes, H, device):
     import torch
     if alibi_slopes is None:
@@ -317,6 +343,7 @@ def flash_attn_bwd(dout, q, k, v, out, lse, softmax_scale=None, causal=False, wi
     if q.dtype != torch.bfloat16:
         raise FA2Error("the backward takes bf16 tensors")
     B, N, H, d = q.shape
+    _check_aux(lse, (B, H, N), q.device, workspace)
     scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     if workspace is None:
@@ -370,6 +397,7 @@ def flash_attn_varlen_bwd(dout, q, k, v, out, lse, cu_seqlens, softmax_scale=Non
         raise FA2Error("packed batches take bf16 tensors")
     T, H, d = q.shape
     cu = _cu(cu_seqlens, q.device)
+    _check_aux(lse, (H, T), q.device, workspace)
     scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     if workspace is None:
@@ -424,6 +452,7 @@ def flash_attn_blocksparse_bwd(dout, q, k, v, out, lse, block_mask, softmax_scal
         raise FA2Error("block-sparse attention takes bf16 tensors")
     B, N, H, d = q.shape
     m, sb, sh = _block_mask(block_mask, B, H, N, q.device)
+    _check_aux(lse, (B, H, N), q.device, workspace)
     scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     if workspace is None:

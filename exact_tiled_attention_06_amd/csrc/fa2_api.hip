@@ -25,6 +25,9 @@ fa2_status_t check_common(int B, int H, int N, int d, float scale, int wl, int w
   if (!(scale > 0.f) || !isfinite(scale)) return FA2_ERR_INVALID_ARG;
   if (wl < -1 || wr < -1) return FA2_ERR_INVALID_ARG;
   if (d != 64 && d != 128) return FA2_ERR_UNSUPPORTED;
+  // Kernels add windows to positions in 32-bit arithmetic; with windows capped
+  // at N - 1 (effective_window) those sums stay below 2N <= 2^31.
+  if (N > (1 << 30)) return FA2_ERR_UNSUPPORTED;
   if ((int64_t)B * H > INT32_MAX) return FA2_ERR_INVALID_ARG;
   // The tile loads address a tile's rows as 32-bit byte offsets from its first row:
   // up to 256 rows of H * d bf16 values must span less than 4 GiB.
@@ -36,6 +39,15 @@ fa2_status_t check_common(int B, int H, int N, int d, float scale, int wl, int w
   return FA2_OK;
 }
 
+// The window the kernels apply for a problem of n tokens (n = total tokens for
+// a packed batch, which bounds every sequence): a side that reaches every key
+// (>= n - 1) becomes -1, so no kernel adds an arbitrarily large window to a
+// position; causal sets the right side to 0. Inputs are already validated.
+void effective_window(int n, int causal, int wl, int wr, int* wl_out, int* wr_out) {
+  *wl_out = (wl < 0 || wl >= n - 1) ? -1 : wl;
+  *wr_out = causal ? 0 : ((wr < 0 || wr >= n - 1) ? -1 : wr);
+}
+
 fa2::FwdParams fwd_params(const void* q, const void* k, const void* v, void* out, float* lse, int B,
                           int H, int N, float scale, int causal, int wl, int wr, const float* alibi) {
   fa2::FwdParams p{};
@@ -44,8 +56,7 @@ fa2::FwdParams fwd_params(const void* q, const void* k, const void* v, void* out
   p.scale = scale;
   p.scale_log2 = scale * fa2::kLog2e;
   p.causal = causal ? 1 : 0;
-  p.wl = wl;
-  p.wr = causal ? 0 : wr;
+  effective_window(N, causal, wl, wr, &p.wl, &p.wr);
   return p;
 }
 
@@ -124,8 +135,7 @@ fa2_status_t bwd_setup(const void* q, const void* k, const void* v, const void* 
   p->scale_log2 = scale * fa2::kLog2e;
   p->inv_scale = 1.0f / scale;
   p->causal = causal ? 1 : 0;
-  p->wl = wl;
-  p->wr = causal ? 0 : wr;
+  effective_window(N, causal, wl, wr, &p->wl, &p->wr);
   return FA2_OK;
 }
 
@@ -391,5 +401,12 @@ const char* fa2_status_string(fa2_status_t s) {
 }
 
 int fa2_version(void) { return kVersion; }
+
+fa2_status_t fa2_effective_window(int n, int causal, int window_left, int window_right, int* left_out,
+                                  int* right_out) {
+  if (n < 0 || window_left < -1 || window_right < -1 || !left_out || !right_out) return FA2_ERR_INVALID_ARG;
+  effective_window(n, causal, window_left, window_right, left_out, right_out);
+  return FA2_OK;
+}
 
 }  // extern "C"

@@ -36,8 +36,9 @@
  *     problem: FA2_OK, nothing launched, pointers not inspected.
  *   - Alignment: every tensor pointer must be 16-byte aligned.
  *   - Supported shapes: d in {64, 128}; any N >= 1 (ragged tails masked);
- *     B * H <= 2^31 - 1; B * N * H * d < 2^62; H * d <= 2^22 (else
- *     FA2_ERR_UNSUPPORTED: tiles are addressed with 32-bit row offsets).
+ *     B * H <= 2^31 - 1; B * N * H * d < 2^62; H * d <= 2^22 and N <= 2^30
+ *     (else FA2_ERR_UNSUPPORTED: tiles are addressed with 32-bit row offsets
+ *     and positions plus windows with 32-bit integers).
  */
 #ifndef FA2_H
 #define FA2_H
@@ -270,6 +271,18 @@ const char* fa2_status_string(fa2_status_t status);
 
 /* Library version as 10000*major + 100*minor + patch. */
 int fa2_version(void);
+
+/*
+ * The window every entry point applies for a problem of n tokens (n = N, or
+ * total_tokens for a packed batch): a side >= n - 1 already reaches every key
+ * and is treated as -1 (unbounded), so windows up to INT_MAX behave like -1;
+ * causal != 0 makes the right side 0. Writes the two values and returns FA2_OK;
+ * FA2_ERR_INVALID_ARG for n < 0, a window < -1 or a null output pointer.
+ * Host-only: touches no device and no stream. Source: window_size of section
+ * 5.1 of the wmrh.cn FlashAttention v2 article (-1 = unbounded).
+ */
+fa2_status_t fa2_effective_window(int n, int causal, int window_left, int window_right,
+                                  int* left_out, int* right_out);
 
 #ifdef __cplusplus
 }

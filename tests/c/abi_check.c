@@ -38,6 +38,15 @@ int main(void) {
   EXPECT(fa2_status_string((fa2_status_t)99) != NULL);
   EXPECT(fa2_version() >= 100);
 
+  /* effective window: a side reaching every key is unbounded, causal clamps the right side */
+  {
+    int l = 7, r = 7;
+    EXPECT(fa2_effective_window(100, 0, 2147483647, 2147483647, &l, &r) == FA2_OK && l == -1 && r == -1);
+    EXPECT(fa2_effective_window(100, 1, 40, 9, &l, &r) == FA2_OK && l == 40 && r == 0);
+    EXPECT(fa2_effective_window(100, 0, -2, 0, &l, &r) == FA2_ERR_INVALID_ARG);
+    EXPECT(fa2_effective_window(100, 0, 0, 0, NULL, &r) == FA2_ERR_INVALID_ARG);
+  }
+
   /* workspace sizes: two per-row float arrays, then the float32 dQ accumulator */
   EXPECT(fa2_bwd_workspace_size(4, 32, 8192, 128) ==
          2 * up256((size_t)4 * 32 * 8192 * 4) + up256((size_t)4 * 32 * 8192 * 128 * 4));

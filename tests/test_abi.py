@@ -33,7 +33,7 @@ def test_header_declares_the_documented_entry_points():
     assert header_functions() == sorted(
         ["fa2_fwd", "fa2_fwd_f32", "fa2_bwd", "fa2_bwd_workspace_size", "fa2_bwd_prep", "fa2_bwd_dkdv",
          "fa2_bwd_dq", "fa2_fwd_varlen", "fa2_bwd_varlen", "fa2_fwd_blocksparse", "fa2_bwd_blocksparse",
-         "fa2_fwd_dropout", "fa2_bwd_dropout", "fa2_status_string", "fa2_version"])
+         "fa2_fwd_dropout", "fa2_bwd_dropout", "fa2_status_string", "fa2_version", "fa2_effective_window"])
 
 
 def test_library_exports_every_header_symbol(lib):
@@ -333,3 +333,32 @@ def test_wrapper_workspace_for_the_atomic_free_backward(lib, monkeypatch):
     assert not fa2._atomic_dq_selected(False)
     monkeypatch.setenv("FA2_BWD_ATOMIC_DQ", "1")
     assert fa2._atomic_dq_selected(False) and not fa2._atomic_dq_selected(True)
+
+
+INT_MAX = 2**31 - 1
+
+
+@pytest.mark.parametrize("n, causal, wl, wr, want", [
+    (100, 0, -1, -1, (-1, -1)),
+    (100, 0, 37, 5, (37, 5)),
+    (100, 0, 98, 98, (98, 98)),        # below n - 1: kept
+    (100, 0, 99, 99, (-1, -1)),        # n - 1 reaches every key
+    (100, 0, INT_MAX, INT_MAX, (-1, -1)),
+    (100, 1, INT_MAX, INT_MAX, (-1, 0)),  # causal: right side 0
+    (100, 1, 50, -1, (50, 0)),
+    (1, 0, 0, 0, (-1, -1)),            # a single token: every window reaches it
+    (0, 0, 5, 5, (-1, -1)),
+])
+def test_effective_window(lib, n, causal, wl, wr, want):
+    assert fa2.fa2_effective_window(n, causal, wl, wr) == want
+
+
+@pytest.mark.parametrize("args", [(-1, 0, -1, -1), (10, 0, -2, -1), (10, 0, -1, -2)])
+def test_effective_window_rejects(lib, args):
+    with pytest.raises(fa2.FA2Error):
+        fa2.fa2_effective_window(*args)
+
+
+def test_huge_n_is_unsupported(lib):
+    st = lib.fa2_fwd(*fwd_args(N=(1 << 30) + 1, B=1, H=1))
+    assert st == fa2.FA2_ERR_UNSUPPORTED

@@ -170,3 +170,41 @@ def test_prep_pass_writes_minus_d_and_minus_lse_over_scale(gpu_lib, d):
     assert np.max(np.abs(nd + d_ref)) <= 1e-4 * max(1.0, np.max(np.abs(d_ref)))
     lse_np = lse.cpu().numpy().astype(np.float64)
     np.testing.assert_allclose(si, -lse_np / scale, rtol=1e-6, atol=1e-6)
+
+
+def test_backward_window_beyond_int_range_is_unbounded(gpu_lib):
+    """window_size = (2^31 - 1, 2^31 - 1) in the backward: bit for bit the gradients of (-1, -1)."""
+    big = 2**31 - 1
+    _, dev, _ = gpu_inputs(1, 2, 300, 128, "bf16", seed=43, with_dout=True)
+    for causal in (False, True):
+        a = run_fwd_bwd(gpu_lib, dev, None, scale_of(128), causal, (big, big), True)
+        b = run_fwd_bwd(gpu_lib, dev, None, scale_of(128), causal, (-1, -1), True)
+        assert all(torch.equal(x, y) for x, y in zip(a, b))
+
+
+@pytest.mark.parametrize("bad", ["bf16", "transposed", "short", "cpu", "workspace_cpu"])
+def test_backward_rejects_a_malformed_lse(gpu_lib, bad):
+    """The wrappers check lse (float32, contiguous, [B, H, N], on the tensors' GPU) and the
+    workspace's device before anything is launched."""
+    B, H, N, d = 1, 2, 64, 64
+    _, dev, _ = gpu_inputs(B, H, N, d, "bf16", seed=44, with_dout=True)
+    out, lse = gpu_lib.flash_attn_fwd(dev["q"], dev["k"], dev["v"], scale_of(d))
+    ws = None
+    if bad == "bf16":
+        lse = lse.to(torch.bfloat16)
+    elif bad == "transposed":
+        lse = lse.transpose(1, 2).contiguous()  # [B, N, H]
+    elif bad == "short":
+        lse = lse[:, :, : N - 1].contiguous()
+    elif bad == "cpu":
+        lse = lse.cpu()
+    else:
+        ws = torch.empty(1 << 16, dtype=torch.uint8)
+    with pytest.raises(gpu_lib.FA2Error):
+        gpu_lib.flash_attn_bwd(dev["dout"], dev["q"], dev["k"], dev["v"], out, lse, scale_of(d), workspace=ws)
+    packed = {k: v.reshape(B * N, H, d) for k, v in dev.items()}
+    cu = torch.tensor([0, N], dtype=torch.int32, device="cuda")
+    o2, l2 = gpu_lib.flash_attn_varlen_fwd(packed["q"], packed["k"], packed["v"], cu, scale_of(d))
+    with pytest.raises(gpu_lib.FA2Error):
+        gpu_lib.flash_attn_varlen_bwd(packed["dout"], packed["q"], packed["k"], packed["v"], o2,
+                                      l2.reshape(1, H, N), cu, scale_of(d))

@@ -102,6 +102,38 @@ def test_fp32_small_masks(gpu_lib, mask):
     assert max_abs(to_np(lse), lse_ref) <= TOL_O_F32
 
 
+@pytest.mark.parametrize("mask", sorted(MASKS))
+def test_fp32_d128_all_outputs(gpu_lib, mask):
+    """The float32-storage forward at d = 128 (the largest register footprint of the
+    float32 kernel) against the oracle, every O and LSE element, within the float32
+    tolerance; shapes span several key tiles and query blocks and end in a ragged tail."""
+    causal, window, alibi = MASKS[mask]
+    B, H, N = 1, 3, 291
+    say(f"fwd f32 d=128 mask={mask} B={B} H={H} N={N}")
+    cpu, dev, slopes = gpu_inputs(B, H, N, 128, "f32", seed=31, alibi=alibi)
+    out, lse = run_fwd(gpu_lib, dev, slopes, scale_of(128), causal, window)
+    o_ref, lse_ref = oracle.attention_forward(cpu["q"], cpu["k"], cpu["v"], scale_of(128), causal, window,
+                                              None if slopes is None else slopes.numpy())
+    eo, el = max_abs(to_np(out), o_ref), max_abs(to_np(lse), lse_ref)
+    say(f"  max|dO|={eo:.3e} max|dLSE|={el:.3e}")
+    assert eo <= TOL_O_F32 and el <= TOL_O_F32
+
+
+@pytest.mark.parametrize("dtype, d", [("bf16", 128), ("bf16", 64), ("f32", 128)])
+def test_window_beyond_int_range_is_unbounded(gpu_lib, dtype, d):
+    """window_size = (2^31 - 1, 2^31 - 1) reaches every key: the result must be the one of
+    (-1, -1), bit for bit (causal and not), and match the oracle's dense result."""
+    big = 2**31 - 1
+    cpu, dev, _ = gpu_inputs(1, 2, 333, d, dtype, seed=41)
+    for causal in (False, True):
+        o1, l1 = run_fwd(gpu_lib, dev, None, scale_of(d), causal, (big, big))
+        o2, l2 = run_fwd(gpu_lib, dev, None, scale_of(d), causal, (-1, -1))
+        assert torch.equal(o1, o2) and torch.equal(l1, l2)
+        o_ref, lse_ref = oracle.attention_forward(cpu["q"], cpu["k"], cpu["v"], scale_of(d), causal)
+        assert max_abs(to_np(o1), o_ref) <= (TOL_O_F32 if dtype == "f32" else TOL_O_BF16)
+        assert max_abs(to_np(l1), lse_ref) <= TOL_LSE
+
+
 @pytest.mark.parametrize("number", [2, 3, 4, 5])
 def test_full_size_workload_sampled_rows(gpu_lib, number):
     w = workloads.WORKLOADS[number]

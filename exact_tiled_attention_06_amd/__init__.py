@@ -30,7 +30,7 @@ import os
 __all__ = [
     "FA2Error", "LIB_PATH", "load_library", "fa2_fwd", "fa2_fwd_f32", "fa2_bwd",
     "fa2_bwd_workspace_size", "fa2_bwd_prep", "fa2_bwd_dkdv", "fa2_bwd_dq", "fa2_fwd_varlen", "fa2_bwd_varlen",
-    "fa2_fwd_blocksparse", "fa2_bwd_blocksparse", "fa2_fwd_dropout", "fa2_bwd_dropout", "fa2_status_string", "fa2_version", "fa2_effective_window", "flash_attn_fwd",
+    "fa2_fwd_blocksparse", "fa2_bwd_blocksparse", "fa2_fwd_dropout", "fa2_bwd_dropout", "fa2_status_string", "fa2_version", "fa2_effective_window", "fa2_bwd_noalloc", "flash_attn_fwd",
     "flash_attn_bwd", "flash_attn_varlen_fwd", "flash_attn_varlen_bwd", "flash_attn_blocksparse_fwd",
     "flash_attn_blocksparse_bwd", "BLOCKSPARSE_BLOCK", "FA2_OK", "FA2_ERR_INVALID_ARG", "FA2_ERR_UNSUPPORTED", "FA2_ERR_HIP",
 ]
@@ -73,6 +73,7 @@ SIGNATURES = {
                          _P, _F, _U64, _U64, _P], _I),
     "fa2_status_string": ([_I], ctypes.c_char_p),
     "fa2_version": ([], _I),
+    "fa2_bwd_noalloc": ([_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _I, _I, _P, _P], _I),
     "fa2_effective_window": ([_I, _I, _I, _I, ctypes.POINTER(_I), ctypes.POINTER(_I)], _I),
 }
 
@@ -130,6 +131,15 @@ def fa2_status_string(status: int) -> str:
 
 def fa2_version() -> int:
     return int(load_library().fa2_version())
+
+
+def fa2_bwd_noalloc(q, k, v, out, lse, dout, dq, dk, dv, B, H, N, d, softmax_scale, causal, window_left,
+                    window_right, alibi_slopes=None, stream=None):
+    st = load_library().fa2_bwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dout), _ptr(dq),
+                                        _ptr(dk), _ptr(dv), int(B), int(H), int(N), int(d), float(softmax_scale),
+                                        int(causal), int(window_left), int(window_right), _ptr(alibi_slopes),
+                                        _stream(stream))
+    _check(st, "fa2_bwd_noalloc")
 
 
 def fa2_effective_window(n, causal, window_left, window_right):

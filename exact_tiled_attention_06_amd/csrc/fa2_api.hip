@@ -6,6 +6,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/fa2.h"
 #include "launch.hpp"
 
@@ -104,6 +106,14 @@ size_t fa2_bwd_workspace_size(int B, int H, int N, int d) {
 
 namespace {
 
+// Workspace: -D per row, -LSE / scale per row, then (atomic dQ only) the dQ accumulator.
+void set_workspace(fa2::BwdParams* p, const void* workspace, size_t rows) {
+  char* ws = reinterpret_cast<char*>(const_cast<void*>(workspace));
+  p->ndelta = reinterpret_cast<float*>(ws);
+  p->s_init = reinterpret_cast<float*>(ws + align256(rows * sizeof(float)));
+  p->dq_acc = reinterpret_cast<float*>(ws + 2 * align256(rows * sizeof(float)));
+}
+
 // Shared validation of the backward entry points; fills the parameter block.
 // need_* say which pointers the entry point reads or writes.
 fa2_status_t bwd_setup(const void* q, const void* k, const void* v, const void* out, const float* lse,
@@ -124,11 +134,7 @@ fa2_status_t bwd_setup(const void* q, const void* k, const void* v, const void* 
   *p = fa2::BwdParams{};
   p->q = q; p->k = k; p->v = v; p->o = out; p->lse = lse; p->dout = dout;
   p->dq = dq; p->dk = dk; p->dv = dv;
-  // Workspace: -D per row, -LSE / scale per row, then (atomic dQ only) the dQ accumulator.
-  char* ws = reinterpret_cast<char*>(const_cast<void*>(workspace));
-  p->ndelta = reinterpret_cast<float*>(ws);
-  p->s_init = reinterpret_cast<float*>(ws + align256(rows * sizeof(float)));
-  p->dq_acc = reinterpret_cast<float*>(ws + 2 * align256(rows * sizeof(float)));
+  set_workspace(p, workspace, rows);
   p->alibi = alibi;
   p->B = B; p->H = H; p->N = N;
   p->scale = scale;
@@ -401,6 +407,67 @@ const char* fa2_status_string(fa2_status_t s) {
 }
 
 int fa2_version(void) { return kVersion; }
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// The allocation-free backward. Its per-row workspace (-D and -LSE / scale, the
+// only scratch the atomic-free backward uses) lives in a file-scope device array
+// that every GPU the library runs on holds until the process ends. Host code
+// never passes the array's name to a kernel (on the host it is only a stand-in):
+// the device address comes from hipGetSymbolAddress, once per device, with that
+// device current, and is kept per device.
+namespace {
+
+constexpr size_t kScratchRows = size_t(1) << 21;                  // B * H * N at most
+constexpr size_t kScratchBytes = 2 * kScratchRows * sizeof(float);  // 16 MiB
+constexpr int kMaxDevices = 64;
+
+}  // namespace
+
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+namespace {
+
+hipError_t scratch_address(void** out) {
+  static std::once_flag once[kMaxDevices];
+  static void* addr[kMaxDevices];
+  static hipError_t err[kMaxDevices];
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::call_once(once[dev], [dev] { err[dev] = hipGetSymbolAddress(&addr[dev], HIP_SYMBOL(scratch)); });
+  if (err[dev] != hipSuccess) return err[dev];
+  *out = addr[dev];
+  return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" {
+
+fa2_status_t fa2_bwd_noalloc(const void* q, const void* k, const void* v, const void* out, const float* lse,
+                             const void* dout, void* dq, void* dk, void* dv, int B, int H, int N, int d,
+                             float softmax_scale, int causal, int window_left, int window_right,
+                             const float* alibi_slopes, void* stream) {
+  bool empty = false;
+  fa2_status_t st = check_common(B, H, N, d, softmax_scale, window_left, window_right, &empty);
+  if (st != FA2_OK || empty) return st;
+  const size_t rows = (size_t)B * H * N;
+  if (rows > kScratchRows) return FA2_ERR_UNSUPPORTED;
+  // Validate every argument before the first HIP call; the stand-in workspace
+  // address is replaced by the device's scratch address below.
+  fa2::BwdParams p;
+  static const char kStandIn alignas(256) = 0;
+  st = bwd_setup(q, k, v, out, lse, dout, dq, dk, dv, &kStandIn, kScratchBytes, stat_bytes(B, H, N), B, H, N, d,
+                 softmax_scale, causal, window_left, window_right, alibi_slopes, true, true, true, true, &p, &empty);
+  if (st != FA2_OK || empty) return st;
+  void* ws = nullptr;
+  if (scratch_address(&ws) != hipSuccess) return FA2_ERR_HIP;
+  set_workspace(&p, ws, rows);
+  return hip_status(fa2::launch_bwd_bf16(p, d, true, (hipStream_t)stream));
+}
 
 fa2_status_t fa2_effective_window(int n, int causal, int window_left, int window_right, int* left_out,
                                   int* right_out) {

@@ -266,6 +266,25 @@ fa2_status_t fa2_bwd_dropout(const void* q, const void* k, const void* v, const 
                              const float* alibi_slopes, float dropout_p, unsigned long long seed,
                              unsigned long long offset, void* stream);
 
+/*
+ * fa2_bwd without a workspace, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc). Same arguments and results as fa2_bwd with deterministic = 1
+ * (the atomic-free passes; bitwise the same gradients), minus workspace and
+ * workspace_bytes. Its per-row scratch (8 bytes per row of B * H * N) lives in a
+ * 16 MiB device array inside the library, one copy per GPU, held until the
+ * process ends; nothing is allocated or freed by the call. Limit:
+ * B * H * N <= 2^21 rows (e.g. B=4, H=32, N=16384), else FA2_ERR_UNSUPPORTED
+ * before any HIP call. Calls that overlap on one GPU (other streams or host
+ * threads) share the array and race: serialise them. Every byte it reads is
+ * written earlier in the same call, so nothing needs clearing between calls.
+ */
+fa2_status_t fa2_bwd_noalloc(const void* q, const void* k, const void* v, const void* out,
+                             const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                             int B, int H, int N, int d, float softmax_scale, int causal,
+                             int window_left, int window_right, const float* alibi_slopes,
+                             void* stream);
+
 /* Static, human-readable name of a status code. */
 const char* fa2_status_string(fa2_status_t status);
 

@@ -38,6 +38,10 @@ int main(void) {
   EXPECT(fa2_status_string((fa2_status_t)99) != NULL);
   EXPECT(fa2_version() >= 100);
 
+  /* the allocation-free backward refuses more rows than its scratch array holds, before any HIP call */
+  EXPECT(fa2_bwd_noalloc(P, P, P, P, F, P, P,
+                         P, P, 4, 32, 16385, 128, 0.088f, 1, -1, -1, NULL, NULL) == FA2_ERR_UNSUPPORTED);
+
   /* effective window: a side reaching every key is unbounded, causal clamps the right side */
   {
     int l = 7, r = 7;

@@ -33,7 +33,8 @@ def test_header_declares_the_documented_entry_points():
     assert header_functions() == sorted(
         ["fa2_fwd", "fa2_fwd_f32", "fa2_bwd", "fa2_bwd_workspace_size", "fa2_bwd_prep", "fa2_bwd_dkdv",
          "fa2_bwd_dq", "fa2_fwd_varlen", "fa2_bwd_varlen", "fa2_fwd_blocksparse", "fa2_bwd_blocksparse",
-         "fa2_fwd_dropout", "fa2_bwd_dropout", "fa2_status_string", "fa2_version", "fa2_effective_window"])
+         "fa2_fwd_dropout", "fa2_bwd_dropout", "fa2_status_string", "fa2_version", "fa2_effective_window",
+         "fa2_bwd_noalloc"])
 
 
 def test_library_exports_every_header_symbol(lib):
@@ -362,3 +363,18 @@ def test_effective_window_rejects(lib, args):
 def test_huge_n_is_unsupported(lib):
     st = lib.fa2_fwd(*fwd_args(N=(1 << 30) + 1, B=1, H=1))
     assert st == fa2.FA2_ERR_UNSUPPORTED
+
+
+def test_noalloc_backward_rejects_before_any_hip_call(lib):
+    """Too many rows for its scratch array, and invalid arguments, are rejected before any
+    HIP call (so on a machine without a GPU too)."""
+    def call(B, H, N, d=128, q=FAKE, scale=0.125):
+        return lib.fa2_bwd_noalloc(q, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, B, H, N, d, scale, 1, -1, -1,
+                                   None, None)
+    assert call(4, 32, 16384 + 1) == fa2.FA2_ERR_UNSUPPORTED   # 2^21 + 128 rows
+    assert call(1, 1, (1 << 21) + 1) == fa2.FA2_ERR_UNSUPPORTED
+    assert call(1, 1, 64, d=96) == fa2.FA2_ERR_UNSUPPORTED
+    assert call(1, 1, 64, q=None) == fa2.FA2_ERR_INVALID_ARG
+    assert call(1, 1, 64, q=MISALIGNED) == fa2.FA2_ERR_INVALID_ARG
+    assert call(1, 1, 64, scale=0.0) == fa2.FA2_ERR_INVALID_ARG
+    assert call(0, 1, 64) == fa2.FA2_OK                        # empty problem

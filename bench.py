@@ -70,19 +70,56 @@ def cpu_baseline(w, min_seconds=10.0, max_heads=16):
         sec += time.perf_counter() - start
         heads += 1
     f_fwd, f_bwd = flops(1, heads, w.N, w.d, w.causal)
+    host = host_info()
     return {
         "value": (f_fwd + f_bwd) / sec / 1e12,
         "unit": "TFLOP/s",
         "cores": blas_threads or len(os.sched_getaffinity(0)),
         "kind": "oracle",
         "sample": f"{heads} of {w.B * w.H} (b,h) heads, full fp64 forward+backward at N={w.N}, d={w.d}, "
-                  f"causal; {sec:.2f} s",
+                  f"causal; {sec:.2f} s measured; the whole workload would take about "
+                  f"{sec * w.B * w.H / heads:.0f} s at this rate (extrapolated)",
         "host_cpus": len(os.sched_getaffinity(0)),
+        "cpu_model": host["cpu_model"],
+        "blas": host["blas"],
+        "blas_threads": blas_threads,
     }
 
 
-def timed(phases, steps, warmup, stream):
-    """Average milliseconds of each (name, fn) phase over `steps` passes, HIP events on `stream`."""
+def host_info():
+    """CPU model (from /proc/cpuinfo) and the BLAS library numpy calls, with its threads."""
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    blas = None
+    try:
+        from threadpoolctl import threadpool_info
+        libs = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if libs:
+            i = libs[0]
+            blas = f"{i.get('internal_api')} {i.get('version')} ({os.path.basename(i.get('filepath', ''))})"
+    except Exception:
+        pass
+    return {"cpu_model": model, "blas": blas}
+
+
+def phase_stats(samples):
+    """Mean, median and min of a list of per-step milliseconds."""
+    xs = sorted(samples)
+    n = len(xs)
+    med = xs[n // 2] if n % 2 else 0.5 * (xs[n // 2 - 1] + xs[n // 2])
+    return {"avg_ms": sum(xs) / n, "median_ms": med, "min_ms": xs[0]}
+
+
+def timed_stats(phases, steps, warmup, stream):
+    """Per-step milliseconds of each (name, fn) phase, HIP events recorded on `stream`
+    (the stream the kernels are launched on) around every launch; returns
+    {name: {avg_ms, median_ms, min_ms}}."""
     import torch
     for _ in range(warmup):
         for _, fn in phases:
@@ -95,7 +132,12 @@ def timed(phases, steps, warmup, stream):
             fn()
             ev[i][n + 1].record(stream)
     torch.cuda.synchronize()
-    return {name: sum(e[n].elapsed_time(e[n + 1]) for e in ev) / steps for n, (name, _) in enumerate(phases)}
+    return {name: phase_stats([e[n].elapsed_time(e[n + 1]) for e in ev]) for n, (name, _) in enumerate(phases)}
+
+
+def timed(phases, steps, warmup, stream):
+    """Average milliseconds of each (name, fn) phase over `steps` passes, HIP events on `stream`."""
+    return {k: v["avg_ms"] for k, v in timed_stats(phases, steps, warmup, stream).items()}
 
 
 def bench_varlen(fa2, workloads, steps, warmup):
@@ -272,6 +314,19 @@ def bench_other_workloads(fa2, workloads, steps, warmup):
     Infinity Cache, so it is also timed with a 512 MB write between launches."""
     import torch
     res = {}
+    # The tiny float32 workload (B=1, H=2, N=128, d=64): latency only (two workgroups).
+    w1 = workloads.WORKLOADS[1]
+    t1 = workloads.make_inputs(w1.B, w1.H, w1.N, w1.d, "f32", seed=w1.number)
+    q1, k1, v1 = (t1[n].cuda() for n in ("q", "k", "v"))
+    o1 = torch.empty_like(q1)
+    l1 = torch.empty((w1.B, w1.H, w1.N), dtype=torch.float32, device="cuda")
+    s1 = torch.cuda.current_stream()
+    st1 = timed_stats([("fwd", lambda: fa2.fa2_fwd_f32(q1, k1, v1, o1, l1, w1.B, w1.H, w1.N, w1.d, w1.scale,
+                                                       int(w1.causal), -1, -1, None, s1.cuda_stream))],
+                      steps, warmup, s1)
+    res[w1.name] = {"workload": w1.describe(), "fwd_us_median": round(1e3 * st1["fwd"]["median_ms"], 2),
+                    "fwd_us_min": round(1e3 * st1["fwd"]["min_ms"], 2)}
+    del q1, k1, v1, o1, l1
     for num in (2, 4, 5):
         w = workloads.WORKLOADS[num]
         B, H, N, d = w.B, w.H, w.N, w.d
@@ -294,17 +349,24 @@ def bench_other_workloads(fa2, workloads, steps, warmup):
         def bwd():
             fa2.fa2_bwd(q, k, v, out, lse, do, dq, dk, dv, ws, ws_bytes, B, H, N, d, w.scale, c, wl, wr, sl, 1, sp)
 
-        ms = timed([("fwd", fwd), ("bwd", bwd)], steps, warmup, stream)
+        st = timed_stats([("fwd", fwd), ("bwd", bwd)], steps, warmup, stream)
+        ms = {k: v["avg_ms"] for k, v in st.items()}
         nominal = 4.0 * B * H * N * N * d * (0.5 if w.causal else 1.0)
         pairs = visible_pairs(B, H, N, w.causal, wl, wr)
+        fwd_alg = 4.0 * d * pairs / (ms["fwd"] * 1e-3) / 1e12
         rec = {
             "workload": w.describe(),
             "fwd_ms": round(ms["fwd"], 4),
             "bwd_ms": round(ms["bwd"], 4),
+            "fwd_ms_median": round(st["fwd"]["median_ms"], 4),
+            "fwd_ms_min": round(st["fwd"]["min_ms"], 4),
+            "bwd_ms_median": round(st["bwd"]["median_ms"], 4),
+            "bwd_ms_min": round(st["bwd"]["min_ms"], 4),
             "fwd_tflops": round(nominal / (ms["fwd"] * 1e-3) / 1e12, 2),
             "bwd_tflops": round(2.5 * nominal / (ms["bwd"] * 1e-3) / 1e12, 2),
-            "fwd_tflops_algorithmic": round(4.0 * d * pairs / (ms["fwd"] * 1e-3) / 1e12, 2),
+            "fwd_tflops_algorithmic": round(fwd_alg, 2),
             "bwd_tflops_algorithmic": round(10.0 * d * pairs / (ms["bwd"] * 1e-3) / 1e12, 2),
+            "fwd_frac_of_peak_algorithmic": round(fwd_alg / PEAK_BF16_TFLOPS, 4),
         }
         if num == 2:
             flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
@@ -344,6 +406,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-other", action="store_true",
+                    help="skip the other dense workloads (d=64 non-causal, N=4096 causal, N=16384 window + ALiBi)")
     ap.add_argument("--no-varlen", action="store_true", help="skip the packed variable-length measurement")
     ap.add_argument("--varlen-only", action="store_true",
                     help="only time the packed variable-length workload (prints its object as the JSON line)")
@@ -452,7 +516,8 @@ def main():
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
     ms_step = total_ms / K
-    ph_ms = {name: sum(e[n].elapsed_time(e[n + 1]) for e in ev) / K for n, (name, _) in enumerate(phases)}
+    ph_stats = {name: phase_stats([e[n].elapsed_time(e[n + 1]) for e in ev]) for n, (name, _) in enumerate(phases)}
+    ph_ms = {name: st["avg_ms"] for name, st in ph_stats.items()}
     f_fwd, f_bwd = flops(B, H, N, d, True)
     pairs = B * H * N * (N + 1) / 2  # visible (query, key) pairs, causal
     fwd_avg = ph_ms["fwd"]
@@ -470,12 +535,14 @@ def main():
     }
     kernels = {}
     for name, ms in ph_ms.items():
-        ent = {"avg_ms": round(ms, 4)}
+        ent = {k: round(v, 4) for k, v in ph_stats[name].items()}
         if name in kinfo:
             kn, fl = kinfo[name]
             ach = fl / (ms * 1e-3) / 1e12
+            ach_med = fl / (ph_stats[name]["median_ms"] * 1e-3) / 1e12
             ent.update({"kernel": kn, "bound": "mfma", "flop_per_launch": fl, "achieved": round(ach, 2),
-                        "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4)})
+                        "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+                        "frac_median": round(ach_med / PEAK_BF16_TFLOPS, 4)})
         kernels[name] = ent
     dom = max((n for n in kernels if "frac" in kernels[n]), key=lambda n: kernels[n]["avg_ms"])
     dk_ = kernels[dom]
@@ -507,6 +574,8 @@ def main():
         "roofline": roofline,
         "kernels": kernels,
     }
+    if not args.no_other:
+        rec["other_workloads"] = bench_other_workloads(fa2, workloads, args.steps, args.warmup)
     if not args.no_varlen:
         rec["varlen"] = bench_varlen(fa2, workloads, args.steps, args.warmup)
     if not args.no_sparse:

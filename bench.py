@@ -16,7 +16,7 @@ width 1 around the diagonal, one global key block and 10 % random blocks,
 about 18 % of the causal blocks) is timed through fa2_fwd_blocksparse /
 fa2_bwd_blocksparse and reported under "blocksparse", counting the visible
 (query, key) pairs of the active blocks. Last, the dense causal workload with
-dropout p = 0.1 on the attention weights (keep matrix from Philox4x64-10,
+dropout p = 0.1 on the attention weights (keep matrix from Philox4x32-10,
 regenerated in the backward) is timed through fa2_fwd_dropout /
 fa2_bwd_dropout and reported under "dropout", with the dense FLOP convention.
 

@@ -42,13 +42,14 @@
 // 128 keys per workgroup, up to two at 256), and a wave whose key block is
 // off skips the tile's compute.
 // DROPOUT (deterministic variant, fixed-length dense batches): the keep
-// matrix of the forward is regenerated from the same Philox4x64-10 counters.
+// matrix of the forward is regenerated from the same Philox4x32-10 counters.
 // With Z the keep matrix and r = 1 / (1 - p): dV = (P * Z)^T dO r,
 // dS = P * (Z * dP r - D), and D = rowsum(dO * O) is unchanged (O is the
 // dropped output). The dQ pass has the forward's query-per-lane layout
-// (keep_bits_qlane); the key-block pass has one key per lane and turns the
-// generator's per-query rows into its columns through 128 bytes of LDS per
-// wave (keep_bits_klane).
+// (keep_words_qlane); the key-block pass has one key per lane: each lane
+// generates half of one query's 32-key row (keep_rows_klane), the halves merge
+// it into 128 bytes of LDS per wave, and each lane reads its key's bits of the
+// block's rows from there.
 #include <type_traits>
 
 #include "common.hpp"
@@ -116,8 +117,15 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p, int zero_acc)
     const int64_t b = row / ((int64_t)p.H * p.N);
     const int64_t bhrow = (b * p.H + h) * p.N + i;
     if (cc == 0) {
-      p.ndelta[bhrow] = -acc;
-      p.s_init[bhrow] = -p.lse[bhrow] * p.inv_scale;
+      if (p.dropout) {
+        // The dropout passes rebuild P r, r = 1 / (1 - p), so ln r joins the exponent, and
+        // start their dP accumulators at -D / r (the dS step below the key-block pass).
+        p.ndelta[bhrow] = -acc * (1.0f / p.drop_scale);
+        p.s_init[bhrow] = (logf(p.drop_scale) - p.lse[bhrow]) * p.inv_scale;
+      } else {
+        p.ndelta[bhrow] = -acc;
+        p.s_init[bhrow] = -p.lse[bhrow] * p.inv_scale;
+      }
     }
     if (zero_acc) {
       f32x4* dst = reinterpret_cast<f32x4*>(p.dq_acc + bhrow * D + cc * 8);
@@ -206,6 +214,7 @@ __global__ __launch_bounds__(NW * 64, ((D == 128 && !DET) ? 4 : 8) / NW) void bw
   const int kj = kw0 + l32;     // key of this lane (MFMA column)
   const int bh = (int)(stat0 / (N > 0 ? N : 1));            // b * H + h (fixed-length batches)
   uint32_t* drop_slot = reinterpret_cast<uint32_t*>(smem + S::LDS) + 32 * w;  // DROPOUT: 32 words per wave
+  const int drop_pos = keep_row_bit(l32);  // DROPOUT: this lane's key in a row mask
 
   // V^T fragments (B operand of dP = dO V^T): lane holds v[kj][16*ks + 8*hh .. +7].
   bf16x8 vf[S::KS];
@@ -428,17 +437,36 @@ __global__ __launch_bounds__(NW * 64, ((D == 128 && !DET) ? 4 : 8) / NW) void bw
         for (int r = 0; r < 16; ++r) pr[r] = visible(r) ? pr[r] : 0.f;
       }
       // Keep bits (dropout) between the two products: S is dead and dP not yet live.
-      const uint32_t keep =
-          DROPOUT ? keep_bits_klane(p.drop_seed, p.drop_offset, p.drop_keep, bh, i0, kw0, l32, hh, drop_slot) : 0u;
+      // One generator call per lane and block: the rows of the block's queries go into
+      // the wave's slot, and each lane reads the bits of its key from there.
+      const uint32_t* keep_rows = drop_slot;
+      if constexpr (DROPOUT) {
+        keep_rows_klane(p.drop_seed_lo, p.drop_seed_hi, p.drop_offset, p.drop_keep, bh, i0, kw0, l32, hh, drop_slot);
+        keep_rows = drop_slot + 8 * hh;
+      }
       // dP - D = dO V^T - D, then dS = P * (dP - D) (under dropout the accumulators start
       // at 0 and dS = P * (Z * dP / (1 - p) - D)).
       f32x16 dp;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) dp[r] = DROPOUT ? 0.f : ndel_t[key_of_reg(r, hh)];
+      for (int r = 0; r < 16; ++r) dp[r] = ndel_t[key_of_reg(r, hh)];
 #pragma unroll
       for (int ks = 0; ks < S::KS; ++ks) {
         const bf16x8 ao = lds_read16_at(kDO + qx[ks]);
         dp = mfma32(ao, vf[ks], dp);
+      }
+      // Under dropout pr holds P r and dp holds dP - D / r, so dS = P (Z dP r - D) is
+      // pr * dp where Z keeps and pr * (-D / r) where it drops; dV takes Z P r. The
+      // -D / r values are read again here, so that they hold no registers across the MFMAs.
+      float nd[16];
+      if constexpr (DROPOUT) {
+        uint32_t nd_addr = kQ + 2 * S::QT_BYTES + S::BQ * 4 + 32 * hh;  // ndel_t + 8 hh
+        opaque(nd_addr);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const f32x4 x = lds_read_f32x4_at(nd_addr + 16 * (c & 1) + 64 * (c >> 1));  // registers 4c .. 4c+3
+#pragma unroll
+          for (int e = 0; e < 4; ++e) nd[4 * c + e] = x[e];
+        }
       }
       bf16x8 pb[2], dsb[2];
 #pragma unroll
@@ -447,9 +475,14 @@ __global__ __launch_bounds__(NW * 64, ((D == 128 && !DET) ? 4 : 8) / NW) void bw
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int r = 8 * kk + e;
-          const bool kept = !DROPOUT || ((keep >> r) & 1u);
-          d8[e] = DROPOUT ? pr[r] * ((kept ? dp[r] * p.drop_scale : 0.f) + ndel_t[key_of_reg(r, hh)]) : pr[r] * dp[r];
-          pk[e] = kept ? pr[r] : 0.f;  // dV takes the kept weights; 1 / (1 - p) is applied at the end
+          if constexpr (DROPOUT) {
+            const uint32_t z = keep_mask_of(drop_row(keep_rows, r), drop_pos);  // all ones: kept
+            d8[e] = pr[r] * select_bits(z, dp[r], nd[r]);
+            pk[e] = select_bits(z, pr[r], 0.f);
+          } else {
+            d8[e] = pr[r] * dp[r];
+            pk[e] = pr[r];
+          }
         }
         pb[kk] = pack_bf16x8(pk[0], pk[1], pk[2], pk[3], pk[4], pk[5], pk[6], pk[7]);
         dsb[kk] = pack_bf16x8(d8[0], d8[1], d8[2], d8[3], d8[4], d8[5], d8[6], d8[7]);
@@ -535,7 +568,7 @@ __global__ __launch_bounds__(NW * 64, ((D == 128 && !DET) ? 4 : 8) / NW) void bw
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           xk[e] = (bf16)(dk[mb][4 * a + e] * p.scale);
-          xv[e] = (bf16)(DROPOUT ? dv[mb][4 * a + e] * p.drop_scale : dv[mb][4 * a + e]);
+          xv[e] = (bf16)dv[mb][4 * a + e];
         }
         *reinterpret_cast<bf16x4*>(dk_row + 32 * mb + 8 * a + 4 * hh) = xk;
         *reinterpret_cast<bf16x4*>(dv_row + 32 * mb + 8 * a + 4 * hh) = xv;
@@ -595,13 +628,14 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_det_kernel(BwdParams p) {  
   // +inf for rows past the end and for rows without a visible key (LSE = -inf): their
   // masked scores (-inf) then give P = exp2(-inf - lse2) = 0 without a NaN.
   const float lse_qi = qi < N ? p.lse[stat0 + qi] : -INFINITY;
-  const float lse2 = lse_qi > -INFINITY ? lse_qi * kLog2e : INFINITY;
-  const float ndelta = qi < N ? p.ndelta[stat0 + qi] : 0.f;  // -D
-  // dP^T accumulators start at -D (every register of a lane holds this lane's query),
-  // so that the MFMAs hand back dP - D; under dropout they start at 0.
+  // Under dropout the pass rebuilds P r, r = 1 / (1 - p): log2 r comes off the statistic.
+  const float lse2 = lse_qi > -INFINITY ? lse_qi * kLog2e - (DROPOUT ? log2f(p.drop_scale) : 0.f) : INFINITY;
+  const float ndelta = qi < N ? p.ndelta[stat0 + qi] : 0.f;  // -D (-D / r under dropout)
+  // dP^T accumulators start at ndelta (every register of a lane holds this lane's query),
+  // so that the MFMAs hand back dP - D (dP - D / r).
   f32x16 dp_init;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) dp_init[r] = DROPOUT ? 0.f : ndelta;
+  for (int r = 0; r < 16; ++r) dp_init[r] = ndelta;
   const float slope2 = ALIBI ? p.alibi[h] * kLog2e : 0.f;
 
   int kv_lo = 0, kv_hi = N;
@@ -693,6 +727,14 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_det_kernel(BwdParams p) {  
       // S^T = K Q^T and dP^T = V dO^T: rows are keys (A lane m reads row kperm(m)), columns queries.
       // The K and V fragments of step ks + 1 are read while the MFMAs of step ks run.
       f32x16 s = f32x16{}, dp = dp_init;
+      if constexpr (DROPOUT) {
+        // Formed per tile: a 16-register copy held across the loop would cost the
+        // generator's registers.
+        float nd = ndelta;
+        opaque(nd);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dp[r] = nd;
+      }
       bf16x8 kv[2][2];
       auto kvload = [&](int ks, bf16x8(&dst)[2]) __attribute__((always_inline)) {
         dst[0] = lds_read16_at(kK + ax[ks]);
@@ -758,14 +800,21 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_det_kernel(BwdParams p) {  
         }
       }
       // dQ^T += K^T dS^T: A = K^T (read above), B = dS^T from registers.
-      const uint32_t keep = DROPOUT ? keep_bits_qlane(p.drop_seed, p.drop_offset, p.drop_keep, bh, qi, j0, hh) : 0u;
+      // Keep words (register r: word keep_word(r), bit keep_bit(r)).
+      uint32_t keep[4] = {};
+      if constexpr (DROPOUT) {
+        keep_words_qlane(p.drop_seed_lo, p.drop_seed_hi, p.drop_offset, p.drop_keep, bh, qi, t, hh, keep);
+#pragma unroll
+        for (int n = 0; n < 4; ++n) opaque(keep[n]);  // unpacked where they are used, not ahead of the MFMAs
+      }
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
         float d8[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int r = 8 * kk + e;
-          d8[e] = DROPOUT ? pr[r] * ((((keep >> r) & 1u) ? dp[r] * p.drop_scale : 0.f) + ndelta) : pr[r] * dp[r];
+          // dropout: pr = P r, dp = dP - D / r; dS = P (Z dP r - D) = pr * (Z ? dp : -D / r)
+          d8[e] = DROPOUT ? pr[r] * select_bits(keep_mask_of(keep[keep_word(r)], keep_bit(r)), dp[r], ndelta) : pr[r] * dp[r];
         }
         const bf16x8 dsb = pack_bf16x8(d8[0], d8[1], d8[2], d8[3], d8[4], d8[5], d8[6], d8[7]);
 #pragma unroll

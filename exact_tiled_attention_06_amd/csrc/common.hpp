@@ -47,6 +47,9 @@ __device__ __forceinline__ bf16x8 lds_read16(const char* base, uint32_t off) {
 __device__ __forceinline__ bf16x8 lds_read16_at(uint32_t addr) {
   return *reinterpret_cast<const bf16x8 FA2_LDS*>((uintptr_t)addr);
 }
+__device__ __forceinline__ f32x4 lds_read_f32x4_at(uint32_t addr) {
+  return *reinterpret_cast<const f32x4 FA2_LDS*>((uintptr_t)addr);
+}
 __device__ __forceinline__ bf16x4 lds_read_tr_at(uint32_t addr) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((bf16x4 FA2_LDS*)((uintptr_t)addr));
 }
@@ -344,58 +347,41 @@ constexpr uint32_t kTileIndexMask = (1u << 14) - 1;
 // Dropout on the attention weights (the dropout_p argument of section 5.1 of
 // the wmrh.cn FlashAttention v2 article; the page names no generator, so the
 // keep matrix is defined here): weight (i, j) of head bh = b * H + h is kept
-// iff a 16-bit value from Philox4x64-10 (Salmon, Moraes, Dror and Shaw,
-// "Parallel random numbers: as easy as 1, 2, 3", SC 2011) is below `keep`.
-// Counter (j / 16, i, bh, 0), key (seed, offset); the 16-bit value of key j
-// is bits 16 * (j % 2) of 32-bit output word (j % 16) / 2 (64-bit words taken
-// low half first). Kept weights are scaled by 1 / (1 - p) where they meet V.
-constexpr uint64_t kPhiloxM0 = 0xD2E7470EE14C6C93ull;
-constexpr uint64_t kPhiloxM1 = 0xCA5A826395121157ull;
-constexpr uint64_t kPhiloxW0 = 0x9E3779B97F4A7C15ull;  // key increments between rounds
-constexpr uint64_t kPhiloxW1 = 0xBB67AE8584CAA73Bull;
+// iff an 8-bit value from Philox4x32-10 (Salmon, Moraes, Dror and Shaw,
+// "Parallel random numbers: as easy as 1, 2, 3", SC 2011) is below `keep`
+// (keep = round(256 (1 - p)), 0 .. 256). Key (seed mod 2^32, seed div 2^32),
+// counter (g, i, bh, offset) with offset < 2^32. A call's sixteen values (its
+// output bytes, little-endian) belong to the keys of the 32-key block c = j / 32
+// with bit 3 of j equal to g % 2, g = 2 c + that bit, in increasing order: key j
+// takes byte 8 ((j / 16) % 2) + j % 8 of group 2 (j / 32) + (j / 8) % 2. These
+// are exactly the keys of one lane half in the query-per-lane layout. Kept
+// weights are scaled by 1 / (1 - p) where they meet V.
+constexpr uint32_t kPhiloxM0 = 0xD2511F53u;
+constexpr uint32_t kPhiloxM1 = 0xCD9E8D57u;
+constexpr uint32_t kPhiloxW0 = 0x9E3779B9u;  // key increments between rounds
+constexpr uint32_t kPhiloxW1 = 0xBB67AE85u;
 
-// Ten rounds; each multiplies two counter words into 128-bit products and
-// mixes the halves with the other two words and the key.
-// The 128-bit product a * M of a 64-bit value and a constant, as its low and
-// high 64-bit halves, from four 32 x 32 -> 64-bit multiply-adds: with
-// a = a1 2^32 + a0 and M = m1 2^32 + m0,
-//   p00 = a0 m0,  p01 = a0 m1 + hi32(p00),  p10 = a1 m0 + lo32(p01),
-//   lo = lo32(p10) 2^32 + lo32(p00),  hi = a1 m1 + hi32(p01) + hi32(p10),
-// where no step overflows 64 bits ((2^32 - 1)^2 + 2 (2^32 - 1) < 2^64).
-template <uint64_t M>
-__device__ __forceinline__ void mulhilo64(uint64_t a, uint64_t& lo, uint64_t& hi) {
-  constexpr uint32_t m0 = (uint32_t)M, m1 = (uint32_t)(M >> 32);
-  const uint32_t a0 = (uint32_t)a, a1 = (uint32_t)(a >> 32);
-  const uint64_t p00 = (uint64_t)a0 * m0;
-  const uint64_t p01 = (uint64_t)a0 * m1 + (p00 >> 32);
-  const uint64_t p10 = (uint64_t)a1 * m0 + (uint32_t)p01;
-  hi = (uint64_t)a1 * m1 + ((p01 >> 32) + (p10 >> 32));
-  lo = (p10 << 32) | (uint32_t)p00;
-}
-
-__device__ __forceinline__ void philox4x64_10(uint64_t c0, uint64_t c1, uint64_t c2, uint64_t c3, uint64_t k0,
-                                              uint64_t k1, uint32_t (&out)[8]) {
+// Ten rounds; each multiplies counter words 0 and 2 by the two constants into
+// 64-bit products and mixes their halves with words 1 and 3 and the key.
+__device__ __forceinline__ void philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3, uint32_t k0,
+                                              uint32_t k1, uint32_t (&out)[4]) {
 #pragma unroll
   for (int r = 0; r < 10; ++r) {
     if (r) {
       k0 += kPhiloxW0;
       k1 += kPhiloxW1;
     }
-    uint64_t lo0, hi0, lo1, hi1;
-    mulhilo64<kPhiloxM0>(c0, lo0, hi0);
-    mulhilo64<kPhiloxM1>(c2, lo1, hi1);
-    const uint64_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
+    const uint64_t p0 = (uint64_t)kPhiloxM0 * c0, p1 = (uint64_t)kPhiloxM1 * c2;
+    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0, n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
     c0 = n0;
-    c1 = lo1;
+    c1 = (uint32_t)p1;
     c2 = n2;
-    c3 = lo0;
+    c3 = (uint32_t)p0;
   }
-  const uint64_t w[4] = {c0, c1, c2, c3};
-#pragma unroll
-  for (int n = 0; n < 4; ++n) {
-    out[2 * n] = (uint32_t)w[n];
-    out[2 * n + 1] = (uint32_t)(w[n] >> 32);
-  }
+  out[0] = c0;
+  out[1] = c1;
+  out[2] = c2;
+  out[3] = c3;
 }
 
 // The same register of the lane 32 apart (lane l <-> l ^ 32). permlane32_swap
@@ -407,59 +393,73 @@ __device__ __forceinline__ uint32_t from_other_half(uint32_t x) {
   return r[0] ^ r[1] ^ x;
 }
 
-// Two keep bits from a 32-bit word of generator output (low half first).
-__device__ __forceinline__ uint32_t keep2(uint32_t word, uint32_t keep) {
-  return ((word & 0xFFFFu) < keep ? 1u : 0u) | ((word >> 16) < keep ? 2u : 0u);
+// Keep bits of a 32-bit word of generator output: bit 8 b + 7 is set iff byte
+// b is below `keep` (0 .. 256), the other bits are zero. The four bytes are
+// compared at once: with h = 0x80 in every byte, (x | h) - (keep & 0x7f) per
+// byte never borrows into the next byte, and its bit 7 says
+// (b & 0x7f) >= (keep & 0x7f); b < keep is then that bit's complement when b and
+// keep agree in bit 7, else keep's bit 7. A host build of this function is
+// checked against a plain byte compare for every byte value, position and
+// threshold.
+__host__ __device__ __forceinline__ uint32_t keep_lt_word(uint32_t x, uint32_t keep) {
+  constexpr uint32_t h = 0x80808080u;
+  if (keep > 255u) return h;  // p = 0: every weight kept
+  const uint32_t lo7 = (keep & 0x7Fu) * 0x01010101u;
+  const uint32_t top = (keep & 0x80u) ? 0u : h;  // bytes where a differing bit 7 decides "not below"
+  const uint32_t d = (x | h) - lo7;
+  return ~((x & d) | ((x ^ d) & top)) & h;
 }
 
 // Query-per-lane layout (S^T = K Q^T, A-operand row kperm(m)): lane (query i,
-// half hh) holds keys j0 + key_of_reg(r, hh) of a 32-key subtile (j0 % 32 == 0).
-// Returns bit r = keep decision of register r. Half 0 runs the generator for
-// keys j0 .. j0+15, half 1 for j0+16 .. j0+31, and each swaps the 8 values the
-// other half needs: registers 0..7 come from the first call, 8..15 from the second.
-__device__ __forceinline__ uint32_t keep_bits_qlane(uint64_t seed, uint64_t offset, uint32_t keep, int bh, int i,
-                                                    int j0, int hh) {
-  uint32_t x[8];
-  philox4x64_10((uint64_t)(j0 / 16 + hh), (uint64_t)(uint32_t)i, (uint64_t)(uint32_t)bh, 0, seed, offset, x);
-  uint32_t bits = 0;
+// half hh) holds keys key_of_reg(r, hh) of the 32-key subtile s, which are the
+// keys of generator group 2 s + hh, register r taking byte r. Returns in w the
+// keep words (keep_lt_word) that hold register r's decision in word keep_word(r)
+// at bit keep_bit(r).
+__device__ __forceinline__ void keep_words_qlane(uint32_t seed_lo, uint32_t seed_hi, uint32_t offset, uint32_t keep,
+                                                 int bh, int i, int s, int hh, uint32_t (&w)[4]) {
+  uint32_t x[4];
+  philox4x32_10((uint32_t)(2 * s + hh), (uint32_t)i, (uint32_t)bh, offset, seed_lo, seed_hi, x);
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const uint32_t recv = from_other_half(hh ? x[k] : x[4 + k]);
-    const uint32_t first = hh ? recv : x[k];       // registers 2k, 2k + 1
-    const uint32_t second = hh ? x[4 + k] : recv;  // registers 8 + 2k, 9 + 2k
-    bits |= keep2(first, keep) << (2 * k);
-    bits |= keep2(second, keep) << (8 + 2 * k);
-  }
-  return bits;
+  for (int n = 0; n < 4; ++n) w[n] = keep_lt_word(x[n], keep);
 }
+__host__ __device__ constexpr int keep_word(int r) { return r >> 2; }
+__host__ __device__ constexpr int keep_bit(int r) { return 8 * (r & 3) + 7; }
 
 // Key-per-lane layout (S = Q K^T, A-operand row kperm(m)): lane (key kw0 + l32,
-// half hh) holds queries i0 + key_of_reg(r, hh); kw0 % 32 == 0. Each lane runs
-// the generator for query i0 + l32 and keys kw0 + 16 hh .. +15; the halves merge
-// into one 32-bit row mask per query, which goes through `slot` (this wave's 32
-// words of LDS) and comes back as the columns. Returns bit r for register r.
-__device__ __forceinline__ uint32_t keep_bits_klane(uint64_t seed, uint64_t offset, uint32_t keep, int bh, int i0,
-                                                    int kw0, int l32, int hh, uint32_t* slot) {
-  uint32_t x[8];
-  philox4x64_10((uint64_t)(kw0 / 16 + hh), (uint64_t)(uint32_t)(i0 + l32), (uint64_t)(uint32_t)bh, 0, seed, offset,
-                x);
+// half hh) holds queries key_of_reg(r, hh) of the 32-query block at i0;
+// kw0 % 32 == 0. Each lane runs the generator for query i0 + l32 and group
+// 2 (kw0 / 32) + hh; the halves merge their bits into the query's 32-key row
+// mask (byte t of group hh' at bit 8 (t % 4) + 4 hh' + t / 4), which goes to
+// slot[l32] (this wave's 32 words of LDS); the block's rows are then read back
+// from the slot.
+__device__ __forceinline__ void keep_rows_klane(uint32_t seed_lo, uint32_t seed_hi, uint32_t offset, uint32_t keep,
+                                                int bh, int i0, int kw0, int l32, int hh, uint32_t* slot) {
+  uint32_t x[4];
+  philox4x32_10((uint32_t)(2 * (kw0 / 32) + hh), (uint32_t)(i0 + l32), (uint32_t)bh, offset, seed_lo, seed_hi, x);
   uint32_t m = 0;
 #pragma unroll
-  for (int k = 0; k < 8; ++k) m |= keep2(x[k], keep) << (2 * k);
+  for (int n = 0; n < 4; ++n) m |= keep_lt_word(x[n], keep) >> (7 - n);  // byte b of word n at bit 8 b + n
   const uint32_t other = from_other_half(m);
-  slot[l32] = hh ? (other | (m << 16)) : (m | (other << 16));  // both halves store the same word
+  slot[l32] = hh ? (other | (m << 4)) : (m | (other << 4));  // both halves store the same word
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  const u32x4 a = *reinterpret_cast<const u32x4*>(slot + 8 * hh);
-  const u32x4 b = *reinterpret_cast<const u32x4*>(slot + 8 * hh + 4);
-  const u32x4 c = *reinterpret_cast<const u32x4*>(slot + 16 + 8 * hh);
-  const u32x4 d = *reinterpret_cast<const u32x4*>(slot + 16 + 8 * hh + 4);
-  const uint32_t rows[16] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3],
-                             c[0], c[1], c[2], c[3], d[0], d[1], d[2], d[3]};
-  uint32_t bits = 0;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) bits |= ((rows[r] >> l32) & 1u) << r;
-  return bits;
+}
+// Bit of key kw0 + l32 in a row mask: byte t = 8 ((l32 / 16) % 2) + l32 % 8 of group (l32 / 8) % 2.
+__device__ __forceinline__ int keep_row_bit(int l32) {
+  const int t = 8 * ((l32 >> 4) & 1) + (l32 & 7);
+  return 8 * (t & 3) + 4 * ((l32 >> 3) & 1) + (t >> 2);
+}
+// Row mask of register r's query: query key_of_reg(r, hh) of the block, from rows = slot + 8 * hh.
+__device__ __forceinline__ uint32_t drop_row(const uint32_t* rows, int r) { return rows[16 * (r >> 3) + (r & 7)]; }
+
+// All ones if bit `pos` of `word` is set, else zero (a sign-extended one-bit field).
+__device__ __forceinline__ uint32_t keep_mask_of(uint32_t word, int pos) {
+  return (uint32_t)__builtin_amdgcn_sbfe((int)word, pos, 1);
+}
+
+// a where mask is all ones, b where it is zero (bitwise, on the float encodings).
+__device__ __forceinline__ float select_bits(uint32_t mask, float a, float b) {
+  return __uint_as_float((__float_as_uint(a) & mask) | (__float_as_uint(b) & ~mask));
 }
 
 struct FwdParams {
@@ -484,7 +484,7 @@ struct FwdParams {
   int dropout;       // 0: no dropout; else keep iff generator value < drop_keep
   uint32_t drop_keep;
   float drop_scale;  // 1 / (1 - p)
-  uint64_t drop_seed, drop_offset;
+  uint32_t drop_seed_lo, drop_seed_hi, drop_offset;
 };
 
 struct BwdParams {
@@ -517,7 +517,7 @@ struct BwdParams {
   int dropout;  // as in FwdParams
   uint32_t drop_keep;
   float drop_scale;
-  uint64_t drop_seed, drop_offset;
+  uint32_t drop_seed_lo, drop_seed_hi, drop_offset;
 };
 
 }  // namespace fa2

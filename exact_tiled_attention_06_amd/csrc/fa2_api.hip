@@ -339,11 +339,13 @@ fa2_status_t fa2_bwd_blocksparse(const void* q, const void* k, const void* v, co
 
 namespace {
 
-// dropout_p in [0, 1): keep threshold floor((1 - p) * 65536 + 0.5) on the
-// generator's 16-bit values, scale 1 / (1 - p). p = 0 keeps every weight and is
+// dropout_p in [0, 1): keep threshold floor((1 - p) * 256 + 0.5) on the
+// generator's 8-bit values, scale 1 / (1 - p). p = 0 keeps every weight and is
 // the dense computation, so it takes the dense kernels.
-fa2_status_t check_dropout(float dropout_p) {
+// offset is the generator's fourth 32-bit counter word, so it must be below 2^32.
+fa2_status_t check_dropout(float dropout_p, unsigned long long offset) {
   if (!(dropout_p >= 0.f) || !(dropout_p < 1.f)) return FA2_ERR_INVALID_ARG;
+  if (offset > 0xFFFFFFFFull) return FA2_ERR_INVALID_ARG;
   return FA2_OK;
 }
 
@@ -351,10 +353,11 @@ template <typename P>
 void set_dropout(P* p, float dropout_p, unsigned long long seed, unsigned long long offset) {
   if (dropout_p == 0.f) return;
   p->dropout = 1;
-  p->drop_keep = (uint32_t)floor((1.0 - (double)dropout_p) * 65536.0 + 0.5);
+  p->drop_keep = (uint32_t)floor((1.0 - (double)dropout_p) * 256.0 + 0.5);
   p->drop_scale = 1.0f / (1.0f - dropout_p);
-  p->drop_seed = seed;
-  p->drop_offset = offset;
+  p->drop_seed_lo = (uint32_t)seed;
+  p->drop_seed_hi = (uint32_t)(seed >> 32);
+  p->drop_offset = (uint32_t)offset;
 }
 
 }  // namespace
@@ -368,7 +371,7 @@ fa2_status_t fa2_fwd_dropout(const void* q, const void* k, const void* v, void* 
   bool empty = false;
   fa2_status_t st = check_common(B, H, N, d, softmax_scale, window_left, window_right, &empty);
   if (st != FA2_OK) return st;
-  if ((st = check_dropout(dropout_p)) != FA2_OK || empty) return st;
+  if ((st = check_dropout(dropout_p, offset)) != FA2_OK || empty) return st;
   if (!q || !k || !v || !out || !lse) return FA2_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(lse))
     return FA2_ERR_INVALID_ARG;
@@ -388,7 +391,7 @@ fa2_status_t fa2_bwd_dropout(const void* q, const void* k, const void* v, const 
   bool empty = false;
   fa2_status_t st = check_common(B, H, N, d, softmax_scale, window_left, window_right, &empty);
   if (st != FA2_OK) return st;
-  if ((st = check_dropout(dropout_p)) != FA2_OK || empty) return st;
+  if ((st = check_dropout(dropout_p, offset)) != FA2_OK || empty) return st;
   st = bwd_setup(q, k, v, out, lse, dout, dq, dk, dv, workspace, workspace_bytes, stat_bytes(B, H, N), B, H, N, d,
                  softmax_scale, causal, window_left, window_right, alibi_slopes, true, true, true, true, &p, &empty);
   if (st != FA2_OK || empty) return st;

@@ -45,9 +45,10 @@
 //    the ring streams only those, so skipped blocks cost neither loads nor
 //    MFMAs. Masks inside a tile are the dense ones.
 //  * DROPOUT: dropout on the attention weights (the dropout_p argument of the
-//    same article, section 5.1). Every lane draws the keep bits of its 16
-//    scores of a 32-key subtile from one Philox4x64-10 call shared with the
-//    other lane half (keep_bits_qlane); the row sum and LSE use the undropped
+//    same article, section 5.1). Each lane runs one Philox4x32-10 call per
+//    32-key subtile, for its query and its own sixteen keys of the subtile
+//    (keep_words_qlane), and masks the packed bf16 weight pairs with pair masks
+//    built by a byte permute; the row sum and LSE use the undropped
 //    weights, the P*V operand the kept ones, and 1 / (1 - p) joins 1 / l in
 //    the epilogue.
 #include <type_traits>
@@ -260,11 +261,14 @@ void fwd_bf16_kernel(FwdParams p) {
         __builtin_amdgcn_sched_group_barrier(0x008, S::NSUB, 0);                       // MFMAs
       });
 
-      // Keep bits of this lane's scores (bit r: register r of subtile sub).
-      uint32_t keep[S::NSUB];
+      // Keep words of this lane's scores (register r of subtile sub: word keep_word(r), bit keep_bit(r)).
+      uint32_t keep[S::NSUB][4] = {};
+      if constexpr (DROPOUT) {
 #pragma unroll
-      for (int sub = 0; sub < S::NSUB; ++sub)
-        keep[sub] = DROPOUT ? keep_bits_qlane(p.drop_seed, p.drop_offset, p.drop_keep, bh, qi, j0 + 32 * sub, hh) : 0u;
+        for (int sub = 0; sub < S::NSUB; ++sub)
+          keep_words_qlane(p.drop_seed_lo, p.drop_seed_hi, p.drop_offset, p.drop_keep, bh, qi, j0 / 32 + sub, hh,
+                           keep[sub]);
+      }
 
       // Bias (ALiBi, in log2 units) and masks; masks only on tiles crossing an edge.
       if (ALIBI) {
@@ -356,10 +360,20 @@ void fwd_bf16_kernel(FwdParams p) {
           const float x = s[sub][8 * kk + e];
           pv[e] = ALIBI ? fast_exp2(x - m2) : fast_exp2(fmaf(x, p.scale_log2, -m2));
         }
-        float pk[8];  // the P*V operand: the kept weights under dropout
+        // The P*V operand: the kept weights under dropout. Registers 8 kk + 4 n' + b are
+        // byte b of keep word 2 kk + n' (bit 7 set: kept); v_perm's sign-of-byte selectors
+        // turn two such bytes into the 0xffff halves that mask one packed bf16 pair.
+        bf16x8 pb = pack_bf16x8(pv[0], pv[1], pv[2], pv[3], pv[4], pv[5], pv[6], pv[7]);
+        if constexpr (DROPOUT) {
+          u32x4 u = __builtin_bit_cast(u32x4, pb);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) pk[e] = DROPOUT ? (((keep[sub] >> (8 * kk + e)) & 1u) ? pv[e] : 0.f) : pv[e];
-        const bf16x8 pb = pack_bf16x8(pk[0], pk[1], pk[2], pk[3], pk[4], pk[5], pk[6], pk[7]);
+          for (int m = 0; m < 4; ++m) {
+            const uint32_t wk = keep[sub][2 * kk + (m >> 1)];
+            // selector 8: sign of byte 1 of (wk << 8) = byte 0 of wk; 9: byte 2; 10: byte 1 of wk; 11: byte 3
+            u[m] &= __builtin_amdgcn_perm(wk, wk << 8, (m & 1) ? 0x0B0B0909u : 0x0A0A0808u);
+          }
+          pb = __builtin_bit_cast(bf16x8, u);
+        }
 #pragma unroll
         for (int e = 0; e < 8; ++e) lsum[e & 3] += pv[e];
 #pragma unroll

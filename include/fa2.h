@@ -232,20 +232,23 @@ fa2_status_t fa2_bwd_blocksparse(const void* q, const void* k, const void* v, co
  * Dropout on the attention weights. The wmrh.cn FlashAttention v2 article
  * (section 5.1, API) lists a dropout_p argument; the page fixes no random
  * number generator, so the keep matrix is defined here:
- *   - weight (i, j) of batch b, head h is kept iff v < keep, where v is a
- *     16-bit value of Philox4x64-10 (Salmon, Moraes, Dror and Shaw, "Parallel
- *     random numbers: as easy as 1, 2, 3", SC 2011) with key (seed, offset)
- *     and counter (j / 16, i, b * H + h, 0): the call's four 64-bit words hold
- *     sixteen 16-bit values, value j % 16 at bits 16 * (j % 4) of word
- *     (j % 16) / 4; keep = floor((1 - dropout_p) * 65536 + 0.5) (dropout_p as
- *     a float, the product in double);
+ *   - weight (i, j) of batch b, head h is kept iff v < keep, where v is an
+ *     8-bit value of Philox4x32-10 (Salmon, Moraes, Dror and Shaw, "Parallel
+ *     random numbers: as easy as 1, 2, 3", SC 2011) with key
+ *     (seed mod 2^32, seed div 2^32) and counter (j / 16, i, b * H + h,
+ *     offset): the call's four 32-bit words hold sixteen 8-bit values, value
+ *     j % 16 at bits 8 * (j % 4) of word (j % 16) / 4;
+ *     keep = floor((1 - dropout_p) * 256 + 0.5) (dropout_p as a float, the
+ *     product in double), so the keep probability keep / 256 resolves
+ *     dropout_p to 1/256;
  *   - O = (P * Z) V / (1 - dropout_p) with P the softmax of the dense
  *     definition (masks and ALiBi as for fa2_fwd); lse is that of the undropped
  *     softmax, so the backward rebuilds P from it as usual;
  *   - the backward regenerates Z from the same seed and offset:
  *     dV = (P * Z)^T dO / (1 - p), dS = P * (Z * dP / (1 - p) - D), with
  *     D = rowsum(dO * O) and O the dropped output the forward wrote.
- * dropout_p must be in [0, 1) (else FA2_ERR_INVALID_ARG); 0 is the dense
+ * dropout_p must be in [0, 1) and offset below 2^32 (else
+ * FA2_ERR_INVALID_ARG); dropout_p = 0 is the dense
  * computation. Distinct (seed, offset) pairs give independent keep matrices;
  * callers advance `offset` between calls that share a seed. Layouts, other
  * arguments and errors as for fa2_fwd / fa2_bwd; the backward is the

@@ -34,5 +34,5 @@ from .dropout import (  # noqa: F401
     dropout_forward_rows,
     keep_rows,
     keep_threshold,
-    philox4x64,
+    philox4x32,
 )

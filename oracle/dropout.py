@@ -14,14 +14,21 @@ the design notes:
     1 - p and the survivors are scaled so that E[O] is the undropped output.
   * The saved statistic is unchanged: LSE is that of the undropped softmax.
   * Z comes from a counter-based generator, so the backward can regenerate it:
-    Philox4x64-10 (Salmon, Moraes, Dror and Shaw, "Parallel random numbers: as
+    Philox4x32-10 (Salmon, Moraes, Dror and Shaw, "Parallel random numbers: as
     easy as 1, 2, 3", SC 2011), with
-      key     = (seed, offset)                              two 64-bit words
-      counter = (j // 16, i, b * H + h, 0)                  four 64-bit words
-    The four 64-bit output words give sixteen 16-bit values; key j of the group
-    takes value t = j % 16, i.e. bits 16 * (t % 4) .. +15 of word t // 4.
-  * Keep iff that value < T, T = floor((1 - p) * 65536 + 0.5) computed in fp64
-    from the fp32 value of p (so p is resolved to 1/65536; p = 0 keeps all).
+      key     = (seed mod 2^32, seed div 2^32)              two 32-bit words
+      counter = (g, i, b * H + h, offset)                   four 32-bit words
+    so offset must be below 2^32. The four 32-bit output words give sixteen
+    8-bit values, the output's bytes in little-endian order (value t: bits
+    8 * (t % 4) .. +7 of word t // 4). Group g holds sixteen keys of the 32-key
+    block c = j // 32: g = 2c for the keys with j % 16 < 8, g = 2c + 1 for the
+    others, each group's keys taking values 0 .. 15 in increasing order; i.e.
+    key j takes value t = 8 * ((j // 16) % 2) + j % 8 of group
+    g = 2 * (j // 32) + (j // 8) % 2. (The split matches the key halves that
+    one lane half of the kernels holds.)
+  * Keep iff that value < T, T = floor((1 - p) * 256 + 0.5) computed in fp64
+    from the fp32 value of p. So the keep probability is T / 256: p is resolved
+    to 1/256 (p = 0 keeps all), and the survivors are still scaled by 1 / (1 - p).
   * Gradients by the chain rule: dV = (P * Z)^T dO / (1 - p);
     dP = Z * (dO V^T) / (1 - p); D = rowsum(P * dP) = rowsum(dO * O);
     dS = P * (dP - D); dQ = scale * dS K; dK = scale * dS^T Q.
@@ -32,66 +39,68 @@ import numpy as np
 
 from . import attention as oa
 
-# Philox4x64 round constants (the SC 2011 paper's multipliers and Weyl increments).
-PHILOX_M0 = 0xD2E7470EE14C6C93
-PHILOX_M1 = 0xCA5A826395121157
-PHILOX_W0 = 0x9E3779B97F4A7C15
-PHILOX_W1 = 0xBB67AE8584CAA73B
+# Philox4x32 round constants (the SC 2011 paper's multipliers and Weyl increments).
+PHILOX_M0 = 0xD2511F53
+PHILOX_M1 = 0xCD9E8D57
+PHILOX_W0 = 0x9E3779B9
+PHILOX_W1 = 0xBB67AE85
 ROUNDS = 10
-KEYS_PER_CALL = 16  # sixteen 16-bit values per call
+KEYS_PER_CALL = 16  # sixteen 8-bit values per call
+VALUE_BITS = 8
 
 _M32 = np.uint64(0xFFFFFFFF)
 _S32 = np.uint64(32)
 
 
-def _mulhilo64(a, b):
-    """Full 128-bit product of uint64 arrays, from 32-bit halves: (hi, lo)."""
-    a0, a1 = a & _M32, a >> _S32
-    b0, b1 = b & _M32, b >> _S32
-    p00, p01, p10, p11 = a0 * b0, a0 * b1, a1 * b0, a1 * b1
-    mid = (p00 >> _S32) + (p01 & _M32) + (p10 & _M32)
-    lo = ((mid & _M32) << _S32) | (p00 & _M32)
-    hi = p11 + (p01 >> _S32) + (p10 >> _S32) + (mid >> _S32)
-    return hi, lo
-
-
-def philox4x64(counter, key, rounds=ROUNDS):
-    """Philox4x64-R on uint64 arrays. counter: [..., 4]; key: (k0, k1). Returns [..., 4]."""
-    c = [np.array(counter, dtype=np.uint64)[..., n].copy() for n in range(4)]
-    k0 = np.uint64(int(key[0]) & 0xFFFFFFFFFFFFFFFF)
-    k1 = np.uint64(int(key[1]) & 0xFFFFFFFFFFFFFFFF)
+def philox4x32(counter, key, rounds=ROUNDS):
+    """Philox4x32-R on arrays of 32-bit words (held in uint64). counter: [..., 4];
+    key: (k0, k1). Each round multiplies counter words 0 and 2 by the two constants
+    into 64-bit products and mixes their halves with words 1 and 3 and the key; the
+    key advances by the Weyl increments between rounds. Returns [..., 4]."""
+    c = [np.array(counter, dtype=np.uint64)[..., n] & _M32 for n in range(4)]
+    k0, k1 = int(key[0]) & 0xFFFFFFFF, int(key[1]) & 0xFFFFFFFF
     m0, m1 = np.uint64(PHILOX_M0), np.uint64(PHILOX_M1)
-    with np.errstate(over="ignore"):
-        for r in range(rounds):
-            if r:
-                k0 = np.uint64((int(k0) + PHILOX_W0) & 0xFFFFFFFFFFFFFFFF)
-                k1 = np.uint64((int(k1) + PHILOX_W1) & 0xFFFFFFFFFFFFFFFF)
-            hi0, lo0 = _mulhilo64(m0, c[0])
-            hi1, lo1 = _mulhilo64(m1, c[2])
-            c = [hi1 ^ c[1] ^ k0, lo1, hi0 ^ c[3] ^ k1, lo0]
+    for r in range(rounds):
+        if r:
+            k0 = (k0 + PHILOX_W0) & 0xFFFFFFFF
+            k1 = (k1 + PHILOX_W1) & 0xFFFFFFFF
+        p0, p1 = m0 * c[0], m1 * c[2]  # below 2^64: no wrap
+        c = [(p1 >> _S32) ^ c[1] ^ np.uint64(k0), p1 & _M32, (p0 >> _S32) ^ c[3] ^ np.uint64(k1), p0 & _M32]
     return np.stack(c, axis=-1)
 
 
 def keep_threshold(dropout_p):
-    """T: a 16-bit value v keeps its weight iff v < T."""
+    """T: an 8-bit value v keeps its weight iff v < T."""
     p = float(np.float32(dropout_p))
     if not 0.0 <= p < 1.0:
         raise ValueError("dropout_p must be in [0, 1)")
-    return int(np.floor((1.0 - p) * 65536.0 + 0.5))
+    return int(np.floor((1.0 - p) * 256.0 + 0.5))
+
+
+def generator_key_counter_word(seed, offset):
+    """(key, fourth counter word) of the stated layout; offset must be below 2^32."""
+    seed, offset = int(seed), int(offset)
+    if not 0 <= offset < 2 ** 32:
+        raise ValueError("offset must be in [0, 2^32)")
+    return (seed & 0xFFFFFFFF, (seed >> 32) & 0xFFFFFFFF), offset
 
 
 def random_values(bh, rows, N, seed, offset):
-    """uint32 [len(rows), N]: the 16-bit value of every (query row, key) of head bh."""
+    """uint32 [len(rows), N]: the 8-bit value of every (query row, key) of head bh."""
+    key, c3 = generator_key_counter_word(seed, offset)
     rows = np.asarray(rows, dtype=np.uint64)
-    groups = np.arange((N + KEYS_PER_CALL - 1) // KEYS_PER_CALL, dtype=np.uint64)
+    j = np.arange(N)
+    g = 2 * (j // 32) + (j // 8) % 2                               # group of key j
+    t = 8 * ((j // 16) % 2) + j % 8                                # its value within the group
+    groups = np.arange(int(g.max()) + 1 if N else 0, dtype=np.uint64)
     ctr = np.zeros((len(rows), len(groups), 4), dtype=np.uint64)
     ctr[..., 0] = groups[None, :]
     ctr[..., 1] = rows[:, None]
     ctr[..., 2] = np.uint64(bh)
-    words = philox4x64(ctr, (seed, offset))                       # [rows, groups, 4]
-    t = np.arange(KEYS_PER_CALL)
-    vals = (words[..., t // 4] >> (np.uint64(16) * (t % 4).astype(np.uint64))) & np.uint64(0xFFFF)
-    return vals.reshape(len(rows), -1)[:, :N].astype(np.uint32)
+    ctr[..., 3] = np.uint64(c3)
+    words = philox4x32(ctr, key)                                   # [rows, groups, 4]
+    vals = (words[:, g, t // 4] >> (np.uint64(VALUE_BITS) * (t % 4).astype(np.uint64))) & np.uint64(0xFF)
+    return vals.astype(np.uint32)
 
 
 def keep_rows(bh, rows, N, dropout_p, seed, offset):

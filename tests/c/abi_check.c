@@ -106,6 +106,9 @@ int main(void) {
   EXPECT(fa2_bwd_dropout(P, P, P, P, F, P, P, P, P, P, 100, 1, 2, 300, 128, 0.125f, 1, -1, -1, NULL, 0.1f, 1, 0,
                          NULL) == FA2_ERR_INVALID_ARG);
   EXPECT(fa2_fwd_dropout(P, P, P, P, F, 0, 2, 300, 128, 0.125f, 1, -1, -1, NULL, 0.1f, 1, 0, NULL) == FA2_OK);
+  /* the offset is the generator's 32-bit counter word */
+  EXPECT(fa2_fwd_dropout(P, P, P, P, F, 0, 2, 300, 128, 0.125f, 1, -1, -1, NULL, 0.1f, 1, 1ull << 32, NULL) ==
+         FA2_ERR_INVALID_ARG);
 
   printf("%d failure(s)\n", failures);
   return failures;

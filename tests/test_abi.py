@@ -271,6 +271,8 @@ BAD_DROPOUT = [
     (dict(scale=0.0), fa2.FA2_ERR_INVALID_ARG),
     (dict(v=None), fa2.FA2_ERR_INVALID_ARG),
     (dict(lse=MISALIGNED), fa2.FA2_ERR_INVALID_ARG),
+    (dict(offset=2**32), fa2.FA2_ERR_INVALID_ARG),  # the generator's counter word is 32 bits
+    (dict(offset=2**64 - 1), fa2.FA2_ERR_INVALID_ARG),
 ]
 
 
@@ -285,6 +287,8 @@ def test_dropout_empty_problem_is_ok(lib, fn):
     assert getattr(lib, fn)(*dropout_args(fn, H=0, q=None)) == fa2.FA2_OK
     # an invalid rate is still rejected on an empty problem
     assert getattr(lib, fn)(*dropout_args(fn, H=0, p=1.5)) == fa2.FA2_ERR_INVALID_ARG
+    assert getattr(lib, fn)(*dropout_args(fn, H=0, offset=2**32)) == fa2.FA2_ERR_INVALID_ARG
+    assert getattr(lib, fn)(*dropout_args(fn, H=0, offset=2**32 - 1, seed=2**64 - 1)) == fa2.FA2_OK
 
 
 def test_dropout_backward_checks_workspace(lib):

@@ -28,3 +28,20 @@ def test_c_program_compiles_links_and_sees_the_documented_status_codes(tmp_path)
     run = subprocess.run([exe], capture_output=True, text=True, timeout=120)
     assert run.returncode == 0, run.stdout + run.stderr
     assert "0 failure(s)" in run.stdout
+
+
+def test_keep_mask_compare_matches_a_plain_byte_compare(tmp_path):
+    """The dropout kernels' packed compare of generator bytes against the keep
+    threshold (tests/c/keep_mask_check.cpp), built for the host only from the
+    kernels' own header: every threshold, byte position and byte value."""
+    hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(hipcc):
+        pytest.skip("no hipcc")
+    exe = str(tmp_path / "keep_mask_check")
+    build = subprocess.run([hipcc, "--cuda-host-only", "-O2", "-std=c++17", "-I",
+                            os.path.join(ROOT, "exact_tiled_attention_06_amd", "csrc"),
+                            os.path.join(ROOT, "tests", "c", "keep_mask_check.cpp"), "-o", exe],
+                           capture_output=True, text=True, timeout=300)
+    assert build.returncode == 0, build.stderr
+    run = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    assert run.returncode == 0 and "0 mismatch(es)" in run.stdout, run.stdout + run.stderr

@@ -1,12 +1,13 @@
-"""Pins for the dropout oracle (keep matrix from Philox4x64-10, weights rescaled by 1/(1-p)).
+"""Pins for the dropout oracle (keep matrix from Philox4x32-10, weights rescaled by 1/(1-p)).
 
 The reading pinned here (wmrh.cn FlashAttention v2 article, section 5.1, names
 dropout_p; the page fixes no generator): O = (softmax(S) * Z) V / (1 - p), LSE
-undropped, Z from Philox4x64-10 with key (seed, offset) and counter
-(j // 16, i, b*H + h, 0), 16-bit value t = j % 16 from bits 16*(t%4) of word t//4,
-kept iff value < floor((1-p)*65536 + 0.5). Checked against:
-* numpy.random.Philox (a library Philox4x64-10; it increments its 256-bit
-  counter before each block, so state c yields the block of counter c + 1);
+undropped, Z from Philox4x32-10 with key (seed mod 2^32, seed div 2^32) and
+counter (g, i, b*H + h, offset), key j taking the 8-bit value t (bits 8*(t%4) of
+word t//4) with g = 2*(j//32) + (j//8)%2 and t = 8*((j//16)%2) + j%8, kept iff
+value < floor((1-p)*256 + 0.5). Checked against:
+* rocRAND's Philox4x32-10 engine (tests/c/philox_ref.cpp, a host build of the
+  library's header), block by block;
 * a keep matrix built in the test from that library generator and the layout
   above, pushed through torch softmax with an explicit additive mask;
 * torch autograd through (softmax(S) * Z) V / (1 - p) for the gradients;
@@ -14,6 +15,12 @@ kept iff value < floor((1-p)*65536 + 0.5). Checked against:
   (the 1/(1-p) rescale), keep-rate and uniformity statistics;
 * planted mistakes, each caught by one of the pins.
 """
+import functools
+import os
+import shutil
+import subprocess
+import tempfile
+
 import numpy as np
 import pytest
 import torch
@@ -21,76 +28,112 @@ import torch
 import oracle
 from oracle import dropout as od
 
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
 
 def rnd(B, N, H, d, seed):
     r = np.random.default_rng(seed)
     return [r.standard_normal((B, N, H, d)) for _ in range(4)]
 
 
-def library_block(counter, key):
-    """Philox4x64-10 block of `counter` from numpy's generator (whose state is one behind)."""
-    c = sum(int(x) << (64 * n) for n, x in enumerate(counter)) - 1
-    c %= 1 << 256
-    words = np.array([(c >> (64 * n)) & ((1 << 64) - 1) for n in range(4)], dtype=np.uint64)
-    g = np.random.Philox(key=np.array([int(key[0]), int(key[1])], dtype=np.uint64), counter=words)
-    return [int(x) for x in g.random_raw(4)]
+@functools.lru_cache(maxsize=None)
+def _reference_program():
+    """Host build of tests/c/philox_ref.cpp against rocRAND's header (cached per session)."""
+    hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(hipcc):
+        pytest.skip("no hipcc for the rocRAND reference generator")
+    exe = os.path.join(tempfile.mkdtemp(prefix="philox_ref_"), "philox_ref")
+    build = subprocess.run([hipcc, "--cuda-host-only", "-O2", "-std=c++17",
+                            os.path.join(ROOT, "tests", "c", "philox_ref.cpp"), "-o", exe],
+                           capture_output=True, text=True, timeout=300)
+    assert build.returncode == 0, build.stderr
+    return exe
+
+
+def library_blocks(jobs):
+    """Philox4x32-10 blocks from rocRAND's engine: jobs = [(counter[4], key[2]), ...]."""
+    text = "".join(" ".join("%x" % (int(x) & 0xFFFFFFFF) for x in (*c, *k)) + "\n" for c, k in jobs)
+    run = subprocess.run([_reference_program()], input=text, capture_output=True, text=True, timeout=120)
+    assert run.returncode == 0, run.stderr
+    return [[int(w, 16) for w in line.split()] for line in run.stdout.splitlines()]
 
 
 def library_keep(bh, N, p, seed, offset):
-    """[N, N] keep matrix of head bh built from numpy's Philox and the stated layout."""
-    T = int(np.floor((1.0 - float(np.float32(p))) * 65536.0 + 0.5))
+    """[N, N] keep matrix of head bh built from rocRAND's Philox and the stated layout."""
+    T = int(np.floor((1.0 - float(np.float32(p))) * 256.0 + 0.5))
+    key = (seed & 0xFFFFFFFF, seed >> 32)
+    groups = 2 * ((N + 31) // 32)
+    blocks = library_blocks([((g, i, bh, offset), key) for i in range(N) for g in range(groups)])
     z = np.zeros((N, N), dtype=bool)
     for i in range(N):
-        for g in range((N + 15) // 16):
-            w = library_block((g, i, bh, 0), (seed, offset))
-            for t in range(16):
-                j = 16 * g + t
+        for g in range(groups):
+            w = blocks[i * groups + g]
+            # group g: the keys of block g // 2 with bit 3 equal to g % 2, in increasing order
+            keys = [32 * (g // 2) + 8 * (g % 2) + 16 * (t // 8) + t % 8 for t in range(16)]
+            for t, j in enumerate(keys):
                 if j < N:
-                    z[i, j] = ((w[t // 4] >> (16 * (t % 4))) & 0xFFFF) < T
+                    z[i, j] = ((w[t // 4] >> (8 * (t % 4))) & 0xFF) < T
     return z
 
 
 # ---------------------------------------------------------------- the generator
 
-@pytest.mark.parametrize("case", range(6))
-def test_philox_matches_numpy_library(case):
-    r = np.random.default_rng(100 + case)
-    key = [int(x) for x in r.integers(0, 2**63, 2)] if case else [0, 0]
-    ctr = [int(x) for x in r.integers(0, 2**63, 4)] if case else [1, 0, 0, 0]
-    ours = od.philox4x64(np.array(ctr, dtype=np.uint64), key)
-    assert [int(x) for x in ours] == library_block(ctr, key)
+def test_philox_matches_rocrand_library():
+    r = np.random.default_rng(100)
+    jobs = [((0, 0, 0, 0), (0, 0)), ((2**32 - 1,) * 4, (2**32 - 1, 2**32 - 1))]
+    jobs += [(tuple(int(x) for x in r.integers(0, 2**32, 4)), tuple(int(x) for x in r.integers(0, 2**32, 2)))
+             for _ in range(30)]
+    ref = library_blocks(jobs)
+    for (c, k), want in zip(jobs, ref):
+        assert [int(x) for x in od.philox4x32(np.array(c, dtype=np.uint64), k)] == want
 
 
 def test_philox_vectorised_over_counters():
-    key = (0x0123456789ABCDEF, 0xFEDCBA9876543210)
-    ctrs = np.array([[g, i, 5, 0] for i in range(3) for g in range(4)], dtype=np.uint64)
-    out = od.philox4x64(ctrs, key)
-    for n, c in enumerate(ctrs):
-        assert [int(x) for x in out[n]] == library_block([int(x) for x in c], key)
+    key = (0x01234567, 0x89ABCDEF)
+    ctrs = np.array([[g, i, 5, 9] for i in range(3) for g in range(4)], dtype=np.uint64)
+    out = od.philox4x32(ctrs, key)
+    ref = library_blocks([([int(x) for x in c], key) for c in ctrs])
+    for n in range(len(ctrs)):
+        assert [int(x) for x in out[n]] == ref[n]
 
 
 def test_value_layout_matches_library_blocks():
-    seed, offset, bh, N = 1234, 7, 3, 40
+    seed, offset, bh, N = 0x1234_0000_5678, 7, 3, 70
     vals = od.random_values(bh, np.arange(5), N, seed, offset)
+    ref = library_blocks([((2 * (j // 32) + (j // 8) % 2, i, bh, offset), (0x5678, 0x1234))
+                          for i in range(5) for j in range(N)])
     for i in range(5):
         for j in range(N):
-            w = library_block((j // 16, i, bh, 0), (seed, offset))
-            t = j % 16
-            assert vals[i, j] == (w[t // 4] >> (16 * (t % 4))) & 0xFFFF
+            w, t = ref[i * N + j], 8 * ((j // 16) % 2) + j % 8
+            assert vals[i, j] == (w[t // 4] >> (8 * (t % 4))) & 0xFF
+    # each group's sixteen values are used once: its keys are a partition of the block
+    for i in range(5):
+        for g in range(4):
+            got = sorted(int(vals[i, j]) for j in range(N) if 2 * (j // 32) + (j // 8) % 2 == g)
+            w = ref[i * N + (32 * (g // 2) + 8 * (g % 2))]
+            assert got == sorted((w[t // 4] >> (8 * (t % 4))) & 0xFF for t in range(16))
+
+
+def test_offset_is_a_32_bit_counter_word():
+    od.random_values(0, [0], 16, 1, 2**32 - 1)
+    for bad in (2**32, -1):
+        with pytest.raises(ValueError):
+            od.random_values(0, [0], 16, 1, bad)
 
 
 @pytest.mark.parametrize("p", [0.1, 0.5, 0.9])
 def test_keep_rate_matches_threshold(p):
     z = od.keep_rows(11, np.arange(512), 512, p, seed=99, offset=0)
     n = z.size
-    q = od.keep_threshold(p) / 65536.0
-    assert abs(q - (1 - p)) <= 2.0 ** -16
+    q = od.keep_threshold(p) / 256.0
+    assert abs(q - (1 - p)) <= 2.0 ** -9
     assert abs(z.mean() - q) < 6 * np.sqrt(q * (1 - q) / n)
 
 
 def test_values_are_uniform_and_heads_independent():
     v = od.random_values(0, np.arange(256), 4096, seed=5, offset=1)
-    hist = np.bincount((v >> 8).ravel(), minlength=256)
+    assert v.max() <= 255
+    hist = np.bincount(v.ravel(), minlength=256)
     e = v.size / 256
     chi2 = float(((hist - e) ** 2 / e).sum())
     assert chi2 < 256 + 8 * np.sqrt(2 * 256)
@@ -103,7 +146,8 @@ def test_values_are_uniform_and_heads_independent():
 
 
 def test_p_zero_keeps_everything():
-    assert od.keep_threshold(0.0) == 65536
+    assert od.keep_threshold(0.0) == 256
+    assert od.keep_threshold(0.999) == 0 and not od.keep_rows(0, np.arange(64), 64, 0.999, 1, 2).any()
     assert od.keep_rows(0, np.arange(64), 64, 0.0, 1, 2).all()
     with pytest.raises(ValueError):
         od.keep_threshold(1.0)
@@ -126,7 +170,7 @@ def slopes(H, on):
 
 
 def torch_with_mask(q, k, v, m, p, seed, offset, scale):
-    """(softmax(S) * Z) V / (1 - p) in torch fp64 with an explicit additive mask and Z from numpy's Philox."""
+    """(softmax(S) * Z) V / (1 - p) in torch fp64 with an explicit additive mask and Z from rocRAND's Philox."""
     B, N, H, d = q.shape
     sl = slopes(H, m["alibi"])
     out = np.zeros_like(q)
@@ -288,13 +332,28 @@ def _m1(mp):
     mp.setattr(od, "keep_rows", f)
 
 
-@_mutant("halfwords_in_reverse_order")
+@_mutant("bytes_in_reverse_order")
 def _m2(mp):
     orig = od.random_values
     def f(bh, rows, N, seed, offset):
-        n16 = (N + 15) // 16 * 16
-        v = orig(bh, rows, n16, seed, offset).reshape(len(rows), -1, 16)[:, :, ::-1]
+        n32 = (N + 31) // 32 * 32
+        v = orig(bh, rows, n32, seed, offset).reshape(len(rows), -1, 32)[:, :, ::-1]
         return v.reshape(len(rows), -1)[:, :N]
+    mp.setattr(od, "random_values", f)
+
+
+@_mutant("consecutive_key_groups")
+def _m2b(mp):
+    def f(bh, rows, N, seed, offset):
+        key, c3 = od.generator_key_counter_word(seed, offset)
+        j = np.arange(N)
+        ctr = np.zeros((len(rows), (N + 15) // 16, 4), dtype=np.uint64)
+        ctr[..., 0] = np.arange((N + 15) // 16)[None, :]
+        ctr[..., 1] = np.asarray(rows)[:, None]
+        ctr[..., 2], ctr[..., 3] = bh, c3
+        w = od.philox4x32(ctr, key)
+        t = j % 16
+        return ((w[:, j // 16, t // 4] >> (8 * (t % 4)).astype(np.uint64)) & 0xFF).astype(np.uint32)
     mp.setattr(od, "random_values", f)
 
 
@@ -326,7 +385,7 @@ def _m6(mp):
 
 @_mutant("threshold_off_by_half")
 def _m7(mp):
-    mp.setattr(od, "keep_threshold", lambda p: int(np.floor((1.0 - float(np.float32(p))) * 32768.0 + 0.5)))
+    mp.setattr(od, "keep_threshold", lambda p: int(np.floor((1.0 - float(np.float32(p))) * 128.0 + 0.5)))
 
 
 def test_unmutated_dropout_oracle_passes_all_pins():

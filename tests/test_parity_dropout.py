@@ -57,10 +57,16 @@ def structured(B, H, N, d, q=None, k=None, v=None, dout=None, seed=0):
 
 # ---------------------------------------------------------------- the keep matrix, bit for bit
 
+# (seed, offset): small values, and a full 64-bit seed with the largest offset
+SEEDS = [(1234, 5), (0xFEDCBA9876543210, 2**32 - 1)]
+
+
+@pytest.mark.parametrize("so", SEEDS)
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
-def test_forward_keep_matrix_is_bitwise_the_oracles(gpu_lib, d, causal):
-    B, H, N, p, seed, offset = 2, 3, d, 0.5, 1234, 5
+def test_forward_keep_matrix_is_bitwise_the_oracles(gpu_lib, d, causal, so):
+    B, H, N, p = 2, 3, d, 0.5
+    seed, offset = so
     say(f"dropout keep matrix, forward d={d} causal={causal}")
     _, dev = structured(B, H, N, d, q=np.zeros((N, d)), v=np.eye(N, d))
     out, _ = gpu_lib.flash_attn_fwd(dev["q"], dev["k"], dev["v"], scale_of(d), causal, dropout_p=p, seed=seed,
@@ -75,9 +81,11 @@ def test_forward_keep_matrix_is_bitwise_the_oracles(gpu_lib, d, causal):
             assert not got[~vis].any()
 
 
+@pytest.mark.parametrize("so", SEEDS)
 @pytest.mark.parametrize("d", [64, 128])
-def test_key_block_pass_keep_matrix_is_bitwise_the_oracles(gpu_lib, d):
-    B, H, N, p, seed, offset = 2, 3, d, 0.5, 99, 1
+def test_key_block_pass_keep_matrix_is_bitwise_the_oracles(gpu_lib, d, so):
+    B, H, N, p = 2, 3, d, 0.5
+    seed, offset = so
     say(f"dropout keep matrix, dK/dV pass d={d}")
     _, dev = structured(B, H, N, d, q=np.zeros((N, d)), dout=np.eye(N, d), seed=3)
     _, _, _, _, dv = run(gpu_lib, dev, None, scale_of(d), False, (-1, -1), p, seed, offset)
@@ -89,9 +97,11 @@ def test_key_block_pass_keep_matrix_is_bitwise_the_oracles(gpu_lib, d):
             assert np.array_equal(g[b, :, h, :].T != 0, z), f"(b, h) = ({b}, {h})"
 
 
+@pytest.mark.parametrize("so", SEEDS)
 @pytest.mark.parametrize("d", [64, 128])
-def test_dq_pass_keep_matrix_is_bitwise_the_oracles(gpu_lib, d):
-    B, H, N, p, seed, offset = 2, 3, d, 0.5, 7, 3
+def test_dq_pass_keep_matrix_is_bitwise_the_oracles(gpu_lib, d, so):
+    B, H, N, p = 2, 3, d, 0.5
+    seed, offset = so
     say(f"dropout keep matrix, dQ pass d={d}")
     e0 = np.zeros((N, d))
     e0[:, 0] = 1.0
@@ -135,11 +145,12 @@ def test_small_dropout(gpu_lib, N, mask, d, p):
     check_small(gpu_lib, 2, 3, N, d, causal, window, alibi, p, seed=81 + d + N)
 
 
-@pytest.mark.parametrize("p", [1e-6, 0.999])
+@pytest.mark.parametrize("p", [1e-6, 0.99, 0.999])
 @pytest.mark.parametrize("N", [1, 17, 200])
 def test_extreme_rates_and_short_sequences(gpu_lib, N, p):
-    # p = 1e-6 keeps every weight (threshold 65536) but still rescales; p = 0.999
-    # keeps about 1 in 1000, so most rows are all-dropped (O = 0, LSE unchanged).
+    # p = 1e-6 keeps every weight (threshold 256) but still rescales; p = 0.99 keeps
+    # 3 in 256 (threshold 3), so most short rows are all-dropped (O = 0, LSE
+    # unchanged); p = 0.999 has threshold 0 and drops every weight.
     # The kept weights are scaled by 1/(1-p), so O and its bf16 rounding error grow
     # by that factor: the absolute O bound is scaled with it.
     say(f"dropout edge N={N} p={p}")

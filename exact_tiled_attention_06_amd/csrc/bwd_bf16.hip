@@ -263,8 +263,9 @@ __global__ __launch_bounds__(NW * 64, ((D == 128 && !DET) ? 4 : 8) / NW) void bw
     const uint8_t* mbh = p.block_mask + (tok0 / N) * p.mask_sb + (int64_t)h * p.mask_sh;
     const int c0 = k0 / kSparseBlock;
     const bool two = S::BK > kSparseBlock && c0 + 1 < p.nbk;
-    n_tiles = compact_tiles(tile_list, it_lo, it_hi, w, [&](int it) -> uint32_t {
-      const uint8_t* row = mbh + (int64_t)((it * S::BQ) / kSparseBlock) * p.nbk + c0;
+    static_assert(kSparseBlock % S::BQ == 0, "whole query tiles per mask block");
+    n_tiles = compact_tiles(tile_list, it_lo, it_hi, kSparseBlock / S::BQ, w, [&](int r) -> uint32_t {
+      const uint8_t* row = mbh + (int64_t)r * p.nbk + c0;  // mask row r: query block r
       return (row[0] != 0 ? 1u : 0u) | (two && row[1] != 0 ? 2u : 0u);
     });
     __syncthreads();
@@ -648,8 +649,9 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_det_kernel(BwdParams p) {  
   int n_tiles = t_hi - t_lo;
   if constexpr (SPARSE) {
     const uint8_t* mrow = p.block_mask + (tok0 / N) * p.mask_sb + (int64_t)h * p.mask_sh + (int64_t)qb * p.nbk;
-    n_tiles = compact_tiles(tile_list, t_lo, t_hi, w,
-                            [&](int t) -> uint32_t { return mrow[(t * BC) / kSparseBlock] != 0 ? 1u : 0u; });
+    static_assert(kSparseBlock % BC == 0, "whole tiles per mask block");
+    n_tiles = compact_tiles(tile_list, t_lo, t_hi, kSparseBlock / BC, w,
+                            [&](int b) -> uint32_t { return mrow[b] != 0 ? 1u : 0u; });
     __syncthreads();
   }
   auto tile_at = [&](int u) __attribute__((always_inline)) -> int {

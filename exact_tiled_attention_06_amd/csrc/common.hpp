@@ -323,21 +323,39 @@ __device__ __forceinline__ int lanes_below(uint64_t bal) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0));
 }
 
-// Compacts the tiles t in [t_lo, t_hi) whose flags (keep(t), two bits) are not
-// zero into list[0 .. n) as t | flags << 14 (LDS, in increasing t; wave 0
-// writes) and returns n. Tile indices must stay below 2^14. Every wave
-// evaluates the same predicates, so n is uniform without a broadcast; the
-// caller synchronises the workgroup before reading the list.
+// Compacts the tiles t in [t_lo, t_hi) of the active blocks (tpb tiles per
+// block; flags(b), two bits, not zero for an active block b) into list[0 .. n)
+// as t | flags << 14 (LDS, in increasing t; wave 0 writes) and returns n. One
+// mask read per lane covers 64 blocks, so a row of up to 64 blocks costs one
+// memory round trip: each lane's block puts its tiles after those of the lanes
+// below it (an inclusive prefix sum across the wave). Tile indices must stay
+// below 2^14. Every wave computes the same n; the caller synchronises the
+// workgroup before reading the list.
 template <typename F>
-__device__ __forceinline__ int compact_tiles(uint16_t* list, int t_lo, int t_hi, int w, F&& keep) {
+__device__ __forceinline__ int compact_tiles(uint16_t* list, int t_lo, int t_hi, int tpb, int w, F&& flags) {
   const int lane = threadIdx.x & 63;
   int n = 0;
-  for (int t0 = t_lo; t0 < t_hi; t0 += 64) {
-    const int t = t0 + lane;
-    const uint32_t f = t < t_hi ? (keep(t) & 3u) : 0u;
-    const uint64_t bal = __builtin_amdgcn_ballot_w64(f != 0);
-    if (w == 0 && f != 0) list[n + lanes_below(bal)] = (uint16_t)(t | (f << 14));
-    n += __builtin_popcountll(bal);
+  if (t_hi <= t_lo) return 0;
+  const int b_lo = t_lo / tpb, b_hi = (t_hi - 1) / tpb + 1;
+  for (int b0 = b_lo; b0 < b_hi; b0 += 64) {
+    const int b = b0 + lane;
+    uint32_t f = 0;
+    int first = 0, c = 0;
+    if (b < b_hi) {
+      f = flags(b) & 3u;
+      first = max(b * tpb, t_lo);
+      c = f != 0 ? min(b * tpb + tpb, t_hi) - first : 0;
+    }
+    int incl = c;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += y;
+    }
+    if (w == 0) {
+      for (int k = 0; k < c; ++k) list[n + incl - c + k] = (uint16_t)((first + k) | (f << 14));
+    }
+    n += __builtin_amdgcn_readlane(incl, 63);
   }
   return n;
 }

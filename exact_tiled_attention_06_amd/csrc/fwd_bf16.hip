@@ -159,8 +159,9 @@ void fwd_bf16_kernel(FwdParams p) {
   if constexpr (SPARSE) {
     const uint8_t* mrow = p.block_mask + (int64_t)(bh / p.H) * p.mask_sb + (int64_t)h * p.mask_sh +
                           (int64_t)qb * p.nbk;
-    n_tiles = compact_tiles(tile_list, t_lo, t_hi, w,
-                            [&](int t) -> uint32_t { return mrow[(t * BC) / kSparseBlock] != 0 ? 1u : 0u; });
+    static_assert(kSparseBlock % BC == 0, "whole tiles per mask block");
+    n_tiles = compact_tiles(tile_list, t_lo, t_hi, kSparseBlock / BC, w,
+                            [&](int b) -> uint32_t { return mrow[b] != 0 ? 1u : 0u; });
     __syncthreads();
   }
   auto tile_at = [&](int u) __attribute__((always_inline)) -> int {

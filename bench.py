@@ -1,8 +1,9 @@
 """Benchmark: exact attention forward + backward on one MI355X.
 
 A step is one pass of the whole hot path over one batch: fa2_fwd then the
-backward's three passes (D = rowsum(dO*O), dK/dV pass, dQ pass; exactly what
-fa2_bwd runs) on the causal N=8192, d=128 bf16 workload (B=4, H=32), inputs
+backward's two passes (the dQ pass, which also forms D = rowsum(dO*O) and the
+per-row values, then the dK/dV pass; exactly what fa2_bwd runs) on the causal
+N=8192, d=128 bf16 workload (B=4, H=32), inputs
 resident in HBM. FLOPs follow the convention of the workload definition:
 forward 4*B*H*N^2*d, halved for causal; backward 2.5x forward. Prints ONE JSON
 line.
@@ -477,21 +478,19 @@ def main():
     def fwd():
         fa2.fa2_fwd(q, k, v, out, lse, B, H, N, d, scale, 1, -1, -1, None, sp)
 
-    # The backward as its three passes (exactly what fa2_bwd runs by default), so
-    # each kernel's duration is measured with its own events.
-    def prep():
-        fa2.fa2_bwd_prep(out, do, lse, ws, ws_bytes, B, H, N, d, scale, sp)
-
+    # The backward as its two passes (exactly what fa2_bwd runs by default: the dQ pass,
+    # which also forms D and the per-row values, then the dK/dV pass), so each kernel's
+    # duration is measured with its own events.
     def dkdv():
         fa2.fa2_bwd_dkdv(q, k, v, lse, do, dk, dv, ws, ws_bytes, B, H, N, d, scale, 1, -1, -1, None, sp)
 
     def dqp():
-        fa2.fa2_bwd_dq(q, k, v, lse, do, dq, ws, ws_bytes, B, H, N, d, scale, 1, -1, -1, None, sp)
+        fa2.fa2_bwd_dq_stats(q, k, v, out, lse, do, dq, ws, ws_bytes, B, H, N, d, scale, 1, -1, -1, None, sp)
 
     def bwd_atomic():
         fa2.fa2_bwd(q, k, v, out, lse, do, dq, dk, dv, ws, ws_bytes, B, H, N, d, scale, 1, -1, -1, None, 0, sp)
 
-    phases = [("fwd", fwd), ("bwd_prep", prep), ("bwd_dkdv", dkdv), ("bwd_dq", dqp)]
+    phases = [("fwd", fwd), ("bwd_dq", dqp), ("bwd_dkdv", dkdv)]
     if args.atomic_dq:
         os.environ["FA2_BWD_ATOMIC_DQ"] = "1"
         phases = [("fwd", fwd), ("bwd_atomic", bwd_atomic)]
@@ -531,7 +530,7 @@ def main():
     kinfo = {
         "fwd": ("fwd_bf16_kernel", 4 * d * pairs),
         "bwd_dkdv": ("bwd_main_kernel (dK, dV)", 8 * d * pairs),
-        "bwd_dq": ("bwd_dq_det_kernel (dQ)", 6 * d * pairs),
+        "bwd_dq": ("bwd_dq_det_kernel (dQ, with D)", 6 * d * pairs),
     }
     kernels = {}
     for name, ms in ph_ms.items():

@@ -29,7 +29,7 @@ import os
 
 __all__ = [
     "FA2Error", "LIB_PATH", "load_library", "fa2_fwd", "fa2_fwd_f32", "fa2_bwd",
-    "fa2_bwd_workspace_size", "fa2_bwd_prep", "fa2_bwd_dkdv", "fa2_bwd_dq", "fa2_fwd_varlen", "fa2_bwd_varlen",
+    "fa2_bwd_workspace_size", "fa2_bwd_prep", "fa2_bwd_dkdv", "fa2_bwd_dq", "fa2_bwd_dq_stats", "fa2_fwd_varlen", "fa2_bwd_varlen",
     "fa2_fwd_blocksparse", "fa2_bwd_blocksparse", "fa2_fwd_dropout", "fa2_bwd_dropout", "fa2_status_string", "fa2_version", "fa2_effective_window", "fa2_bwd_noalloc", "flash_attn_fwd",
     "flash_attn_bwd", "flash_attn_varlen_fwd", "flash_attn_varlen_bwd", "flash_attn_blocksparse_fwd",
     "flash_attn_blocksparse_bwd", "BLOCKSPARSE_BLOCK", "FA2_OK", "FA2_ERR_INVALID_ARG", "FA2_ERR_UNSUPPORTED", "FA2_ERR_HIP",
@@ -62,6 +62,8 @@ SIGNATURES = {
     "fa2_bwd_prep": ([_P, _P, _P, _P, ctypes.c_size_t, _I, _I, _I, _I, _F, _P], _I),
     "fa2_bwd_dkdv": ([_P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _I, _I, _I, _I, _F, _I, _I, _I, _P, _P], _I),
     "fa2_bwd_dq": ([_P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _I, _I, _I, _I, _F, _I, _I, _I, _P, _P], _I),
+    "fa2_bwd_dq_stats": ([_P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _I, _I, _I, _I, _F, _I, _I, _I, _P, _P],
+                         _I),
     "fa2_fwd_varlen": ([_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _I, _I, _P, _P], _I),
     "fa2_bwd_varlen": ([_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _I, _I, _I, _I, _F, _I, _I, _I,
                         _P, _P], _I),
@@ -203,6 +205,15 @@ def fa2_bwd_dq(q, k, v, lse, dout, dq, workspace, workspace_bytes, B, H, N, d, s
                                    int(causal), int(window_left), int(window_right), _ptr(alibi_slopes),
                                    _stream(stream))
     _check(st, "fa2_bwd_dq")
+
+
+def fa2_bwd_dq_stats(q, k, v, out, lse, dout, dq, workspace, workspace_bytes, B, H, N, d, softmax_scale, causal,
+                     window_left, window_right, alibi_slopes=None, stream=None):
+    st = load_library().fa2_bwd_dq_stats(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dout), _ptr(dq),
+                                         _ptr(workspace), int(workspace_bytes), int(B), int(H), int(N), int(d),
+                                         float(softmax_scale), int(causal), int(window_left), int(window_right),
+                                         _ptr(alibi_slopes), _stream(stream))
+    _check(st, "fa2_bwd_dq_stats")
 
 
 def fa2_fwd_varlen(q, k, v, out, lse, cu_seqlens, B, total_tokens, H, d, softmax_scale, causal, window_left,

@@ -31,7 +31,10 @@
 //  3. bwd_dq_convert_kernel: dQ = scale * accumulator, rounded to bf16.
 // Deterministic variant: pass 2 skips dQ, and bwd_dq_det_kernel forms dQ per
 // 128-query block by a key sweep shaped like the forward (S^T = K Q^T,
-// dP^T = V dO^T, dQ^T += K^T dS^T), with no atomics.
+// dP^T = V dO^T, dQ^T += K^T dS^T), with no atomics. The full backward runs it
+// first, with pass 1 folded in: it holds each query's dO row anyway, so it also
+// loads the O row, forms D in pass 1's order of operations and writes both
+// per-row values; then pass 2 runs. The separate pass entry points keep pass 1.
 // VARLEN (packed sequences of different lengths, deterministic variant only):
 // as in the forward, workgroups cover an upper bound of the blocks present and
 // find their sequence with varlen_block; D and LSE are [H, total tokens].
@@ -631,7 +634,36 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_det_kernel(BwdParams p) {  
   const float lse_qi = qi < N ? p.lse[stat0 + qi] : -INFINITY;
   // Under dropout the pass rebuilds P r, r = 1 / (1 - p): log2 r comes off the statistic.
   const float lse2 = lse_qi > -INFINITY ? lse_qi * kLog2e - (DROPOUT ? log2f(p.drop_scale) : 0.f) : INFINITY;
-  const float ndelta = qi < N ? p.ndelta[stat0 + qi] : 0.f;  // -D (-D / r under dropout)
+  float ndelta;  // -D (-D / r under dropout)
+  if (p.fuse_stats) {
+    // D = rowsum(dO * O) of this lane's query, and the two per-row values the key-block
+    // pass reads, in bwd_pre_kernel's order of operations so that they are bit for bit
+    // its values: an 8-element dot product per 16-byte chunk (chunk 2 ks + hh here),
+    // then sums of chunks c and c ^ off for off = d / 16 .. 1 (the last across halves).
+    const bf16* og = (const bf16*)p.o + base;
+    float part[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const bf16x8 o8 = qi < N ? *reinterpret_cast<const bf16x8*>(og + (int64_t)qi * rs + 16 * ks + 8 * hh) : bf16x8{};
+      float acc = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc = fmaf((float)o8[e], (float)of[ks][e], acc);
+      part[ks] = acc;
+    }
+#pragma unroll
+    for (int half = KS / 2; half >= 1; half >>= 1) {
+#pragma unroll
+      for (int ks = 0; ks < half; ++ks) part[ks] += part[ks + half];
+    }
+    const float dsum = part[0] + __uint_as_float(from_other_half(__float_as_uint(part[0])));
+    ndelta = p.dropout ? -dsum * (1.0f / p.drop_scale) : -dsum;
+    if (hh == 0 && qi < N) {
+      p.ndelta[stat0 + qi] = ndelta;
+      p.s_init[stat0 + qi] = p.dropout ? (logf(p.drop_scale) - lse_qi) * p.inv_scale : -lse_qi * p.inv_scale;
+    }
+  } else {
+    ndelta = qi < N ? p.ndelta[stat0 + qi] : 0.f;
+  }
   // dP^T accumulators start at ndelta (every register of a lane holds this lane's query),
   // so that the MFMAs hand back dP - D (dP - D / r).
   f32x16 dp_init;
@@ -978,9 +1010,12 @@ hipError_t launch_bwd_dq(const BwdParams& p, int d, hipStream_t stream) {
 hipError_t launch_bwd_bf16(const BwdParams& p, int d, bool split_dq, hipStream_t stream) {
   hipError_t e;
   if (split_dq) {
-    if ((e = launch_bwd_prep(p, d, false, stream)) != hipSuccess) return e;
-    if ((e = launch_bwd_dkdv(p, d, stream)) != hipSuccess) return e;
-    return launch_bwd_dq(p, d, stream);
+    // The dQ pass forms D and the per-row values itself (they equal the D pass's bit for
+    // bit), so it runs first and the key-block pass reads what it wrote.
+    BwdParams pq = p;
+    pq.fuse_stats = 1;
+    if ((e = launch_bwd_dq(pq, d, stream)) != hipSuccess) return e;
+    return launch_bwd_dkdv(p, d, stream);
   }
   if (p.cu_seqlens != nullptr || p.block_mask != nullptr || p.dropout) return hipErrorInvalidValue;  // split dQ only
   if ((e = launch_bwd_prep(p, d, true, stream)) != hipSuccess) return e;

@@ -536,6 +536,7 @@ struct BwdParams {
   uint32_t drop_keep;
   float drop_scale;
   uint32_t drop_seed_lo, drop_seed_hi, drop_offset;
+  int fuse_stats;  // dQ pass: form D and write ndelta, s_init itself (needs o), instead of reading them
 };
 
 }  // namespace fa2

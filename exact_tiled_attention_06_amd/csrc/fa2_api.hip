@@ -215,6 +215,20 @@ fa2_status_t fa2_bwd_dq(const void* q, const void* k, const void* v, const float
   return hip_status(fa2::launch_bwd_dq(p, d, (hipStream_t)stream));
 }
 
+fa2_status_t fa2_bwd_dq_stats(const void* q, const void* k, const void* v, const void* out, const float* lse,
+                              const void* dout, void* dq, void* workspace, size_t workspace_bytes, int B, int H,
+                              int N, int d, float softmax_scale, int causal, int window_left, int window_right,
+                              const float* alibi_slopes, void* stream) {
+  fa2::BwdParams p;
+  bool empty = false;
+  fa2_status_t st = bwd_setup(q, k, v, out, lse, dout, dq, nullptr, nullptr, workspace, workspace_bytes,
+                              stat_bytes(B, H, N), B, H, N, d, softmax_scale, causal, window_left, window_right,
+                              alibi_slopes, true, true, true, false, &p, &empty);
+  if (st != FA2_OK || empty) return st;
+  p.fuse_stats = 1;
+  return hip_status(fa2::launch_bwd_dq(p, d, (hipStream_t)stream));
+}
+
 }  // extern "C"
 
 namespace {

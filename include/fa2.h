@@ -116,10 +116,11 @@ fa2_status_t fa2_bwd(const void* q, const void* k, const void* v, const void* ou
                      int deterministic, void* stream);
 
 /*
- * The three passes of fa2_bwd's default (atomic-free) algorithm as separate
- * calls, for callers that schedule them themselves (for instance the dK/dV
- * and dQ passes on two streams: both depend only on fa2_bwd_prep; on MI355X
- * the two in order on one stream measured faster). Arguments
+ * The three passes of the atomic-free backward as separate calls, for callers
+ * that schedule them themselves (for instance the dK/dV and dQ passes on two
+ * streams: both depend only on fa2_bwd_prep). fa2_bwd itself runs the two-call
+ * form fa2_bwd_dq_stats then fa2_bwd_dkdv (below), which saves the extra read
+ * of dO. Arguments
  * mean what they mean for fa2_bwd; the same workspace (at least
  * 2 * round_up(4 * B * H * N, 256) bytes) must be passed to all three, with the
  * same lse and softmax_scale, and fa2_bwd_prep must have completed before the
@@ -147,6 +148,23 @@ fa2_status_t fa2_bwd_dq(const void* q, const void* k, const void* v, const float
                         int B, int H, int N, int d, float softmax_scale, int causal,
                         int window_left, int window_right, const float* alibi_slopes,
                         void* stream);
+
+/*
+ * The dQ pass with fa2_bwd_prep folded in, as fa2_bwd runs it: besides dQ it
+ * forms D = rowsum(dO * O) for every query row it covers and writes -D and
+ * -LSE / scale into the workspace, bit for bit what fa2_bwd_prep writes, so
+ * that fa2_bwd_dkdv can follow it (on the same stream, or after it completes).
+ * fa2_bwd's default algorithm is exactly fa2_bwd_dq_stats then fa2_bwd_dkdv.
+ * Arguments as for fa2_bwd_dq, plus out (the forward's output, [B, N, H, d]
+ * bf16); the workspace is written. Errors as for fa2_bwd_dq (out null or
+ * misaligned: FA2_ERR_INVALID_ARG).
+ * Source: the backward-by-recomputation of "AI基础 | Flash Attention"
+ * (section 反向传播); D is the rowsum term of its dS formula.
+ */
+fa2_status_t fa2_bwd_dq_stats(const void* q, const void* k, const void* v, const void* out, const float* lse,
+                              const void* dout, void* dq, void* workspace, size_t workspace_bytes, int B,
+                              int H, int N, int d, float softmax_scale, int causal, int window_left,
+                              int window_right, const float* alibi_slopes, void* stream);
 
 /*
  * Variable-length batches: B sequences of different lengths packed along the

@@ -32,7 +32,7 @@ def lib():
 def test_header_declares_the_documented_entry_points():
     assert header_functions() == sorted(
         ["fa2_fwd", "fa2_fwd_f32", "fa2_bwd", "fa2_bwd_workspace_size", "fa2_bwd_prep", "fa2_bwd_dkdv",
-         "fa2_bwd_dq", "fa2_fwd_varlen", "fa2_bwd_varlen", "fa2_fwd_blocksparse", "fa2_bwd_blocksparse",
+         "fa2_bwd_dq", "fa2_bwd_dq_stats", "fa2_fwd_varlen", "fa2_bwd_varlen", "fa2_fwd_blocksparse", "fa2_bwd_blocksparse",
          "fa2_fwd_dropout", "fa2_bwd_dropout", "fa2_status_string", "fa2_version", "fa2_effective_window",
          "fa2_bwd_noalloc"])
 
@@ -150,6 +150,12 @@ def test_pass_entry_points_reject_bad_arguments(lib):
     assert lib.fa2_bwd_dq(*dq_args[:5], None, *dq_args[6:]) == fa2.FA2_ERR_INVALID_ARG      # dq null
     assert lib.fa2_bwd_dq(*dq_args[:14], -3, *dq_args[15:]) == fa2.FA2_ERR_INVALID_ARG     # window
     assert lib.fa2_bwd_dq(*dq_args[:11], 128 + 1, *dq_args[12:]) == fa2.FA2_ERR_UNSUPPORTED
+    st_args = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws, 1, 2, 16, 64, 0.125, 1, -1, -1, None, None]
+    assert lib.fa2_bwd_dq_stats(*st_args[:3], None, *st_args[4:]) == fa2.FA2_ERR_INVALID_ARG  # out null
+    assert lib.fa2_bwd_dq_stats(*st_args[:3], MISALIGNED, *st_args[4:]) == fa2.FA2_ERR_INVALID_ARG
+    assert lib.fa2_bwd_dq_stats(*st_args[:8], 4, *st_args[9:]) == fa2.FA2_ERR_INVALID_ARG  # workspace
+    assert lib.fa2_bwd_dq_stats(*st_args[:12], 96, *st_args[13:]) == fa2.FA2_ERR_UNSUPPORTED
+    assert lib.fa2_bwd_dq_stats(*st_args[:9], 0, *st_args[10:]) == fa2.FA2_OK  # empty
 
 
 def varlen_fwd_args(**over):

@@ -150,6 +150,31 @@ def test_pass_entry_points_match_fa2_bwd_on_two_streams(gpu_lib, d):
 
 
 @pytest.mark.parametrize("d", [64, 128])
+def test_fused_dq_pass_writes_the_prep_values_and_matches_fa2_bwd(gpu_lib, d):
+    """fa2_bwd_dq_stats writes the workspace fa2_bwd_prep writes, bit for bit, and
+    fa2_bwd_dq_stats then fa2_bwd_dkdv equal fa2_bwd bitwise."""
+    B, H, N = 2, 3, 450
+    cpu, dev, slopes = gpu_inputs(B, H, N, d, "bf16", seed=46, with_dout=True, alibi=True)
+    sl = slopes.cuda()
+    scale = scale_of(d)
+    out, lse = gpu_lib.flash_attn_fwd(dev["q"], dev["k"], dev["v"], scale, True, (200, 0), sl)
+    ref = gpu_lib.flash_attn_bwd(dev["dout"], dev["q"], dev["k"], dev["v"], out, lse, scale, True, (200, 0), sl)
+    ws_bytes = 2 * ((B * H * N * 4 + 255) // 256 * 256)
+    ws_prep = torch.full((ws_bytes,), 0x7F, dtype=torch.uint8, device="cuda")
+    ws = torch.full((ws_bytes,), 0x7F, dtype=torch.uint8, device="cuda")
+    gpu_lib.fa2_bwd_prep(out, dev["dout"], lse, ws_prep, ws_bytes, B, H, N, d, scale, None)
+    dq, dk, dv = (torch.empty_like(dev["q"]) for _ in range(3))
+    gpu_lib.fa2_bwd_dq_stats(dev["q"], dev["k"], dev["v"], out, lse, dev["dout"], dq, ws, ws_bytes, B, H, N, d,
+                             scale, 1, 200, 0, sl, None)
+    gpu_lib.fa2_bwd_dkdv(dev["q"], dev["k"], dev["v"], lse, dev["dout"], dk, dv, ws, ws_bytes, B, H, N, d, scale,
+                         1, 200, 0, sl, None)
+    torch.cuda.synchronize()
+    assert torch.equal(ws, ws_prep)
+    for x, y in zip((dq, dk, dv), ref):
+        assert torch.equal(x, y)
+
+
+@pytest.mark.parametrize("d", [64, 128])
 def test_prep_pass_writes_minus_d_and_minus_lse_over_scale(gpu_lib, d):
     """fa2_bwd_prep's workspace: -D per row (D = rowsum(dO * O), fp64 from the given O
     and dO) at offset 0, then -LSE / scale per row, each array rounded up to 256 bytes."""

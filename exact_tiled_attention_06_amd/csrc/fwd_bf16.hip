@@ -164,11 +164,15 @@ void fwd_bf16_kernel(FwdParams p) {
                             [&](int b) -> uint32_t { return mrow[b] != 0 ? 1u : 0u; });
     __syncthreads();
   }
+  // Under ALiBi the sweep runs from the last tile down: the bias grows toward the
+  // diagonal, so an ascending sweep would raise the row maximum on nearly every tile
+  // (and rescale O each time); descending, the first tiles already hold it.
   auto tile_at = [&](int u) __attribute__((always_inline)) -> int {
+    const int k = ALIBI ? n_tiles - 1 - u : u;
     if constexpr (SPARSE) {
-      return __builtin_amdgcn_readfirstlane((int)(tile_list[u] & kTileIndexMask));
+      return __builtin_amdgcn_readfirstlane((int)(tile_list[k] & kTileIndexMask));
     } else {
-      return t_lo + u;
+      return t_lo + k;
     }
   };
 

@@ -83,7 +83,7 @@ fa2_status_t fa2_fwd_f32(const float* q, const float* k, const float* v, float* 
  * arrays [B, H, N], -D (D = rowsum(dO * O)) at offset 0 and -LSE / scale after
  * it, then a float32 dQ accumulator [B, H, N, d] used only by the atomic
  * variant (each part rounded up to 256 bytes). The default fa2_bwd and the
- * three pass entry points below only touch the two per-row arrays,
+ * pass entry points below only touch the two per-row arrays,
  * 2 * round_up(4 * B * H * N, 256) bytes, and accept a workspace of that size.
  * Returns 0 for an empty or invalid shape.
  */
@@ -101,7 +101,8 @@ size_t fa2_bwd_workspace_size(int B, int H, int N, int d);
  * workspace_bytes says how much was given; too little is FA2_ERR_INVALID_ARG);
  * its contents need not be initialised and are overwritten.
  * deterministic != 0 guarantees bitwise-repeatable results: dQ is
- * formed by a separate pass over query blocks, without atomics. With
+ * formed by a separate pass over query blocks, without atomics (it runs
+ * first and also forms D; then the dK/dV pass). With
  * deterministic = 0 the library may choose; it currently uses the same pass
  * (the faster one on MI355X). Setting the environment variable
  * FA2_BWD_ATOMIC_DQ=1 makes deterministic = 0 accumulate dQ with float32
@@ -200,7 +201,8 @@ fa2_status_t fa2_fwd_varlen(const void* q, const void* k, const void* v, void* o
  * Backward of fa2_fwd_varlen (same arguments, plus dout, dq, dk, dv and a
  * workspace of at least 2 * round_up(4 * H * total_tokens, 256) bytes, which
  * fa2_bwd_workspace_size(1, H, total_tokens, d) covers). Always the
- * atomic-free algorithm (D pass, dK/dV pass, dQ pass): bitwise repeatable.
+ * atomic-free algorithm (the dQ pass, which also forms D, then the dK/dV
+ * pass): bitwise repeatable.
  */
 fa2_status_t fa2_bwd_varlen(const void* q, const void* k, const void* v, const void* out,
                             const float* lse, const void* dout, void* dq, void* dk, void* dv,

@@ -116,6 +116,79 @@ def test_dq_pass_keep_matrix_is_bitwise_the_oracles(gpu_lib, d, so):
             assert np.array_equal(g[b, :, h, :] > 0, z), f"(b, h) = ({b}, {h})"
 
 
+# Far from the origin: a causal window of 128 keys (window_left = 127) with uniform weights
+# (q = 0) and one-hot rows by position mod 128 make every output element carry exactly one
+# keep bit, so whole keep matrices at N = 2048 (generator groups up to 127, rows up to 2047)
+# are compared bit for bit in all three kernels.
+NFAR, DFAR, WFAR = 2048, 128, 127
+FAR_SEED, FAR_OFFSET = 0x0123456789ABCDEF, 2**31 + 12345
+
+
+def residue_rows(N, d):
+    r = np.zeros((N, d))
+    r[np.arange(N), np.arange(N) % d] = 1.0
+    return r
+
+
+def far_run(gpu_lib, **pats):
+    _, dev = structured(1, 2, NFAR, DFAR, seed=5, **pats)
+    return run(gpu_lib, dev, None, scale_of(DFAR), True, (WFAR, 0), 0.5, FAR_SEED, FAR_OFFSET)
+
+
+def key_of_residue(i, c):
+    """The key of row i's window [i - 127, i] congruent to c mod 128, or -1."""
+    j = i - ((i - c) % 128)
+    return j if j >= 0 else -1
+
+
+def test_forward_keep_matrix_far_from_the_origin(gpu_lib):
+    say("dropout keep matrix, forward, N=2048 window 128")
+    out, _, _, _, _ = far_run(gpu_lib, q=np.zeros((NFAR, DFAR)), v=residue_rows(NFAR, DFAR))
+    o = to_np(out)
+    for h in range(2):
+        z = keep_matrix(h, NFAR, 0.5, FAR_SEED, FAR_OFFSET)
+        i, c = np.meshgrid(np.arange(NFAR), np.arange(DFAR), indexing="ij")
+        j = i - ((i - c) % 128)
+        want = np.where(j >= 0, z[i, np.maximum(j, 0)], False)
+        assert np.array_equal(o[0, :, h, :] != 0, want), f"head {h}"
+
+
+def test_key_block_pass_keep_matrix_far_from_the_origin(gpu_lib):
+    say("dropout keep matrix, dK/dV pass, N=2048 window 128")
+    _, _, _, _, dv = far_run(gpu_lib, q=np.zeros((NFAR, DFAR)), dout=residue_rows(NFAR, DFAR))
+    g = to_np(dv)
+    for h in range(2):
+        z = keep_matrix(h, NFAR, 0.5, FAR_SEED, FAR_OFFSET)
+        j, c = np.meshgrid(np.arange(NFAR), np.arange(DFAR), indexing="ij")
+        i = j + ((c - j) % 128)  # the query of key j's window [j, j + 127] congruent to c
+        want = np.where(i < NFAR, z[np.minimum(i, NFAR - 1), j], False)
+        # dV_j[c] = P Z / (1 - p) for that query: non-zero iff (query, key) kept
+        assert np.array_equal(g[0, :, h, :] != 0, want), f"head {h}"
+
+
+def test_dq_pass_keep_matrix_far_from_the_origin(gpu_lib):
+    say("dropout keep matrix, dQ pass, N=2048 window 128")
+    e0 = np.zeros((NFAR, DFAR))
+    e0[:, 0] = 1.0
+    _, _, dq, _, _ = far_run(gpu_lib, q=np.zeros((NFAR, DFAR)), k=residue_rows(NFAR, DFAR), v=e0, dout=e0)
+    g = to_np(dq)
+    for h in range(2):
+        z = keep_matrix(h, NFAR, 0.5, FAR_SEED, FAR_OFFSET)
+        checked = 0
+        for i in range(NFAR):
+            lo = max(0, i - WFAR)
+            kept = int(z[i, lo:i + 1].sum())
+            if kept == 0 or kept == i + 1 - lo:
+                continue  # D equals every kept weight's value (or none is kept): dS is 0
+            for c in range(DFAR):
+                j = key_of_residue(i, c)
+                # dQ_i[c] = scale dS_ij = scale P (Z / (1 - p) - D_i), 0 < D_i < 1 / (1 - p)
+                assert (g[0, i, h, c] > 0) == (j >= 0 and bool(z[i, j])), f"head {h} row {i} col {c}"
+                assert j >= 0 or g[0, i, h, c] == 0
+            checked += 1
+        assert checked > NFAR - 20
+
+
 # ---------------------------------------------------------------- values against the oracle
 
 def check_small(fa2, B, H, N, d, causal, window, alibi, p, seed, o_tol=TOL_O_BF16):

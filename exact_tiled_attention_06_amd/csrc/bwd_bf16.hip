@@ -686,11 +686,13 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_det_kernel(BwdParams p) {  
                             [&](int b) -> uint32_t { return mrow[b] != 0 ? 1u : 0u; });
     __syncthreads();
   }
+  // Key tiles from the last down, as in the forward: with the longest blocks
+  // started first, late workgroups read the tiles their neighbours are reading.
   auto tile_at = [&](int u) __attribute__((always_inline)) -> int {
     if constexpr (SPARSE) {
-      return __builtin_amdgcn_readfirstlane((int)(tile_list[u] & kTileIndexMask));
+      return __builtin_amdgcn_readfirstlane((int)(tile_list[n_tiles - 1 - u] & kTileIndexMask));
     } else {
-      return t_lo + u;
+      return t_hi - 1 - u;
     }
   };
 
@@ -863,7 +865,7 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_det_kernel(BwdParams p) {  
     constexpr int k = decltype(sc)::value;
     if (k < n_tiles) issue(tile_at(k), std::integral_constant<int, k>{});
   });
-  wait_ring<NST, 2 * PER_WAVE>(n_tiles - 1);  // tile 0 has landed
+  wait_ring<NST, 2 * PER_WAVE>(n_tiles - 1);  // the first tile to visit has landed
   for (int u = 0; u < n_tiles; u += NST) {
     static_for<0, NST>([&](auto sc) {
       constexpr int k = decltype(sc)::value;

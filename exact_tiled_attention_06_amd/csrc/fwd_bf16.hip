@@ -164,11 +164,14 @@ void fwd_bf16_kernel(FwdParams p) {
                             [&](int b) -> uint32_t { return mrow[b] != 0 ? 1u : 0u; });
     __syncthreads();
   }
-  // Under ALiBi the sweep runs from the last tile down: the bias grows toward the
-  // diagonal, so an ascending sweep would raise the row maximum on nearly every tile
-  // (and rescale O each time); descending, the first tiles already hold it.
+  // The sweep runs from the last tile down. Blocks start longest first, so a
+  // workgroup that starts when another ends reads the tiles its running
+  // neighbours of the same head are reading, and K/V come from L2 rather than
+  // HBM again (an ascending sweep restarts every late workgroup at tile 0).
+  // Under ALiBi the bias grows toward the diagonal, so the first tiles also hold
+  // the row maximum and O is rarely rescaled.
   auto tile_at = [&](int u) __attribute__((always_inline)) -> int {
-    const int k = ALIBI ? n_tiles - 1 - u : u;
+    const int k = n_tiles - 1 - u;
     if constexpr (SPARSE) {
       return __builtin_amdgcn_readfirstlane((int)(tile_list[k] & kTileIndexMask));
     } else {
@@ -394,7 +397,7 @@ void fwd_bf16_kernel(FwdParams p) {
     constexpr int k = decltype(sc)::value;
     if (k < n_tiles) issue(tile_at(k), std::integral_constant<int, k>{});
   });
-  wait_ring<NST, S::VM_PER_TILE>(n_tiles - 1);  // tile 0 has landed
+  wait_ring<NST, S::VM_PER_TILE>(n_tiles - 1);  // the first tile to visit has landed
   for (int u = 0; u < n_tiles; u += NST) {
     static_for<0, NST>([&](auto sc) {
       constexpr int k = decltype(sc)::value;

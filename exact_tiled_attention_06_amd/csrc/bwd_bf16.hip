@@ -686,8 +686,9 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_det_kernel(BwdParams p) {  
                             [&](int b) -> uint32_t { return mrow[b] != 0 ? 1u : 0u; });
     __syncthreads();
   }
-  // Key tiles from the last down, as in the forward: with the longest blocks
-  // started first, late workgroups read the tiles their neighbours are reading.
+  // Key tiles from the last down: with the longest blocks started first, a
+  // workgroup that starts when another ends reads tiles its running neighbours
+  // read shortly before (for this pass it missed L2 less than ascending).
   auto tile_at = [&](int u) __attribute__((always_inline)) -> int {
     if constexpr (SPARSE) {
       return __builtin_amdgcn_readfirstlane((int)(tile_list[n_tiles - 1 - u] & kTileIndexMask));

@@ -60,9 +60,10 @@ namespace fa2 {
 
 constexpr float kRescaleLog2 = 8.0f;
 #ifndef FA2_HEAD_GROUP
-#define FA2_HEAD_GROUP 4
+#define FA2_HEAD_GROUP 2
 #endif
-constexpr int kHeadGroup = FA2_HEAD_GROUP;  // heads walked together per XCD
+// Heads walked together per XCD: pairs of neighbouring heads.
+constexpr int kHeadGroup = FA2_HEAD_GROUP;
 
 template <int D, int NW, int BC, int NST>
 struct FwdShape {
@@ -104,7 +105,7 @@ void fwd_bf16_kernel(FwdParams p) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
   int bh, qb;
-  grid_map<kHeadGroup>((int)blockIdx.x, p.n_qblocks, p.B * p.H, true, bh, qb);  // longest blocks first
+  grid_map<kHeadGroup, true>((int)blockIdx.x, p.n_qblocks, p.B * p.H, true, bh, qb);  // longest first
   int h, N;
   int64_t tok0, stat0;  // first token of the sequence; index of its row 0 in lse
   if constexpr (VARLEN) {
@@ -164,14 +165,14 @@ void fwd_bf16_kernel(FwdParams p) {
                             [&](int b) -> uint32_t { return mrow[b] != 0 ? 1u : 0u; });
     __syncthreads();
   }
-  // The sweep runs from the last tile down. Blocks start longest first, so a
-  // workgroup that starts when another ends reads the tiles its running
-  // neighbours of the same head are reading, and K/V come from L2 rather than
-  // HBM again (an ascending sweep restarts every late workgroup at tile 0).
-  // Under ALiBi the bias grows toward the diagonal, so the first tiles also hold
-  // the row maximum and O is rarely rescaled.
+  // Tiles in ascending order: the workgroups of a head that start together read
+  // each K/V tile at about the same time, so it is fetched once into L2 (with
+  // the pairs of neighbouring heads per XCD this missed least of the orders and
+  // groupings measured). Under ALiBi the sweep runs from the last tile down: the
+  // bias grows toward the diagonal, so an ascending sweep would raise the row
+  // maximum on nearly every tile (and rescale O each time).
   auto tile_at = [&](int u) __attribute__((always_inline)) -> int {
-    const int k = n_tiles - 1 - u;
+    const int k = ALIBI ? n_tiles - 1 - u : u;
     if constexpr (SPARSE) {
       return __builtin_amdgcn_readfirstlane((int)(tile_list[k] & kTileIndexMask));
     } else {

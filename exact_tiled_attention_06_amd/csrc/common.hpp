@@ -255,7 +255,7 @@ __device__ __forceinline__ void opaque(T& x) {
 // `descending`: block index runs nblk-1 .. 0 (causal forward: long blocks are
 // the late query blocks); else 0 .. nblk-1 (causal backward: early key blocks).
 template <int G, bool NEIGHBOURS = false>
-__device__ __forceinline__ void grid_map(int id, int nblk, int bh_count, bool descending, int& bh, int& blk) {
+__host__ __device__ __forceinline__ void grid_map(int id, int nblk, int bh_count, bool descending, int& bh, int& blk) {
   int r;
   if ((bh_count & 7) == 0 && ((bh_count >> 3) % G) == 0) {
     const int xcd = id & 7, s = id >> 3;

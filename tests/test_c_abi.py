@@ -45,3 +45,20 @@ def test_keep_mask_compare_matches_a_plain_byte_compare(tmp_path):
     assert build.returncode == 0, build.stderr
     run = subprocess.run([exe], capture_output=True, text=True, timeout=120)
     assert run.returncode == 0 and "0 mismatch(es)" in run.stdout, run.stdout + run.stderr
+
+
+def test_grid_map_covers_every_head_and_block_once(tmp_path):
+    """The kernels' workgroup-to-(head, block) map (tests/c/grid_map_check.cpp),
+    built for the host only from the kernels' own header: a bijection for every head
+    group size, head order, block order and a range of head and block counts."""
+    hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(hipcc):
+        pytest.skip("no hipcc")
+    exe = str(tmp_path / "grid_map_check")
+    build = subprocess.run([hipcc, "--cuda-host-only", "-O2", "-std=c++17", "-I",
+                            os.path.join(ROOT, "exact_tiled_attention_06_amd", "csrc"),
+                            os.path.join(ROOT, "tests", "c", "grid_map_check.cpp"), "-o", exe],
+                           capture_output=True, text=True, timeout=300)
+    assert build.returncode == 0, build.stderr
+    run = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    assert run.returncode == 0 and "0 failure(s)" in run.stdout, run.stdout + run.stderr

@@ -29,7 +29,9 @@
 //    the MFMAs of tile t, and one barrier per tile hands a stage over. LDS rows
 //    are XOR-swizzled in 16-byte chunks so that the 16-byte K reads and the
 //    transposed V reads are free of bank conflicts.
-//  * Causal / windowed grids run the longest query blocks first; masks are
+//  * Causal / windowed grids run the longest query blocks first, and each XCD
+//    walks two neighbouring heads at a time (grid_map), so the workgroups of a
+//    head that run together share its K/V tiles in their XCD's L2; masks are
 //    evaluated only on tiles that cross a mask edge or the end of the sequence.
 //  * VARLEN: sequences of different lengths packed along the token axis (the
 //    variable-length batches of the wmrh.cn FlashAttention v2 article, section

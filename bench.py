@@ -546,8 +546,15 @@ def main():
     dom = max((n for n in kernels if "frac" in kernels[n]), key=lambda n: kernels[n]["avg_ms"])
     dk_ = kernels[dom]
     traffic = recorded_traffic(dom)
+    # Compulsory HBM bytes per launch: each tensor of B*N*H*d bf16 values read or
+    # written once, plus the per-row fp32 statistics.
+    tb, sb = B * N * H * d * 2, B * H * N * 4
+    compulsory = {"fwd": 3 * tb + (tb + sb), "bwd_dq": (5 * tb + sb) + (tb + 2 * sb),
+                  "bwd_dkdv": (4 * tb + 2 * sb) + 2 * tb}[dom]
     roofline = {"bound": "mfma", "achieved": dk_["achieved"], "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": dk_["frac"], "traffic": traffic, "kernel": dk_["kernel"], "call": dom}
+                "frac": dk_["frac"], "traffic": traffic, "kernel": dk_["kernel"], "call": dom,
+                "compulsory_bytes": compulsory,
+                "traffic_over_compulsory": None if traffic is None else round(traffic / compulsory, 3)}
 
     rec = {
         "metric": METRIC,

@@ -35,8 +35,9 @@ fa2_status_t check_common(int B, int H, int N, int d, float scale, int wl, int w
   // up to 256 rows of H * d bf16 values must span less than 4 GiB.
   if ((int64_t)H * d > (int64_t)1 << 22) return FA2_ERR_UNSUPPORTED;
   if ((double)B * N * H * d >= 4.6e18) return FA2_ERR_INVALID_ARG;
-  // grid: ceil(N / 64) * B * H blocks must fit a 32-bit grid dimension
-  if ((int64_t)((N + 63) / 64) * B * H > (int64_t)UINT32_MAX) return FA2_ERR_UNSUPPORTED;
+  // grid: ceil(N / 64) * B * H blocks (the most any kernel launches) must fit the
+  // signed 32-bit workgroup id the kernels map to (head, block)
+  if ((int64_t)((N + 63) / 64) * B * H > (int64_t)INT32_MAX) return FA2_ERR_UNSUPPORTED;
   if (B == 0 || H == 0 || N == 0) *empty = true;
   return FA2_OK;
 }

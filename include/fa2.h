@@ -36,9 +36,10 @@
  *     problem: FA2_OK, nothing launched, pointers not inspected.
  *   - Alignment: every tensor pointer must be 16-byte aligned.
  *   - Supported shapes: d in {64, 128}; any N >= 1 (ragged tails masked);
- *     B * H <= 2^31 - 1; B * N * H * d < 2^62; H * d <= 2^22 and N <= 2^30
- *     (else FA2_ERR_UNSUPPORTED: tiles are addressed with 32-bit row offsets
- *     and positions plus windows with 32-bit integers).
+ *     B * H <= 2^31 - 1; B * N * H * d < 2^62; H * d <= 2^22, N <= 2^30 and
+ *     ceil(N / 64) * B * H <= 2^31 - 1 (else FA2_ERR_UNSUPPORTED: tiles are
+ *     addressed with 32-bit row offsets, positions plus windows with 32-bit
+ *     integers, and workgroups by a signed 32-bit id).
  */
 #ifndef FA2_H
 #define FA2_H

@@ -375,6 +375,11 @@ def test_huge_n_is_unsupported(lib):
     assert st == fa2.FA2_ERR_UNSUPPORTED
 
 
+def test_grid_beyond_a_signed_32_bit_workgroup_id_is_unsupported(lib):
+    # 2^24 blocks of 64 rows per head times 129 heads: 2^31 + 2^24 workgroups
+    assert lib.fa2_fwd(*fwd_args(N=1 << 30, B=129, H=1, d=64)) == fa2.FA2_ERR_UNSUPPORTED
+
+
 def test_noalloc_backward_rejects_before_any_hip_call(lib):
     """Too many rows for its scratch array, and invalid arguments, are rejected before any
     HIP call (so on a machine without a GPU too)."""
